@@ -1,0 +1,137 @@
+"""Checks shared by the tests: golden-file parsing, optimality conditions, the
+weighted objective and the GPU-versus-oracle parity rule.
+
+None of this computes the fit; it only judges one.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_cases(name: str):
+    """Parse a golden file into dicts with keys case, source, y, w, z (Fractions)."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            val = val.strip()
+            if key == "case":
+                cur = {"case": val}
+                cases.append(cur)
+            elif key == "source":
+                cur["source"] = val
+            elif key in ("y", "z", "S"):
+                cur[key] = [Fraction(t) for t in val.split()]
+            elif key == "w":
+                cur["w"] = None if val == "-" else [Fraction(t) for t in val.split()]
+    return cases
+
+
+def read_single(name: str):
+    """Parse a golden file without case headers (key: values lines)."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            out[key] = [Fraction(t) for t in val.split()]
+    return out
+
+
+def objective(y, w, z) -> float:
+    """sum_i w_i (z_i - y_i)^2 in f64 (paper section 2.1, equation (1))."""
+    y = np.asarray(y, np.float64)
+    z = np.asarray(z, np.float64)
+    w = np.ones_like(y) if w is None else np.asarray(w, np.float64)
+    return float(np.sum(w * (z - y) ** 2))
+
+
+def objective_gap(y, w, out, z) -> float:
+    """f(out) - f(z), formed term by term as w (o - z)(o + z - 2y) to avoid cancellation."""
+    y = np.asarray(y, np.float64)
+    z = np.asarray(z, np.float64)
+    o = np.asarray(out, np.float64)
+    w = np.ones_like(y) if w is None else np.asarray(w, np.float64)
+    return float(np.sum(w * (o - z) * (o + z - 2.0 * y)))
+
+
+def kkt_violation(y, w, z) -> dict:
+    """Optimality conditions of the isotonic fit, in units of sum w|y| (at least 1).
+
+    With lambda_k = sum_{i<=k} w_i (y_i - z_i):  lambda_k >= 0 for all k,
+    lambda_n = 0, lambda_k = 0 wherever z_{k+1} > z_k, and z non-decreasing
+    (Mova groupant card, entries "Invariant" and "kkt_prefix").
+    """
+    y = np.asarray(y, np.float64)
+    z = np.asarray(z, np.float64)
+    w = np.ones_like(y) if w is None else np.asarray(w, np.float64)
+    scale = max(1.0, float(np.sum(w * np.abs(y))))
+    lam = np.cumsum(w * (y - z))
+    rise = np.zeros(len(y), bool)
+    rise[:-1] = z[1:] > z[:-1]
+    return {
+        "neg_prefix": float(max(0.0, -lam.min())) / scale if len(lam) else 0.0,
+        "total": abs(float(lam[-1])) / scale if len(lam) else 0.0,
+        "at_rise": float(np.abs(lam[rise]).max()) / scale if rise.any() else 0.0,
+        "step_down": float(max(0.0, -(np.diff(z).min() if len(z) > 1 else 0.0))),
+    }
+
+
+def kkt_ok(y, w, z, tau=1e-12) -> bool:
+    v = kkt_violation(y, w, z)
+    return v["neg_prefix"] <= tau and v["total"] <= tau and v["at_rise"] <= tau and v["step_down"] == 0.0
+
+
+def parity(y, w, out, z64, rel_obj=1e-9):
+    """The GPU-versus-oracle rule, per row:
+    max |out - z| <= 1e-5 (1 + max|y|), and |f(out) - f(z)| <= 1e-9 max(f(z), 2^-24 sum w y^2).
+    Returns (ok, worst_abs_ratio, worst_obj_ratio, row_of_worst)."""
+    y = np.atleast_2d(np.asarray(y, np.float64))
+    out = np.atleast_2d(np.asarray(out, np.float64))
+    z64 = np.atleast_2d(np.asarray(z64, np.float64))
+    wr = None if w is None else np.atleast_2d(np.asarray(w, np.float64))
+    worst_a, worst_o, worst_row = 0.0, 0.0, -1
+    for r in range(y.shape[0]):
+        wrow = None if wr is None else wr[r]
+        tol = 1e-5 * (1.0 + float(np.abs(y[r]).max()))
+        a = float(np.abs(out[r] - z64[r]).max()) / tol if y.shape[1] else 0.0
+        fz = objective(y[r], wrow, z64[r])
+        wy2 = float(np.sum((np.ones_like(y[r]) if wrow is None else wrow) * y[r] ** 2))
+        den = max(fz, 2.0 ** -24 * wy2, 1e-300)
+        o = abs(objective_gap(y[r], wrow, out[r], z64[r])) / (rel_obj * den)
+        if max(a, o) > max(worst_a, worst_o):
+            worst_row = r
+        worst_a, worst_o = max(worst_a, a), max(worst_o, o)
+    return (worst_a <= 1.0 and worst_o <= 1.0), worst_a, worst_o, worst_row
+
+
+def block_ids_consistent(oracle_bid, gpu_bid, z64, y, delta_scale=1e-6) -> bool:
+    """Every oracle block start whose adjacent means differ by more than delta is a
+    GPU block start, and every extra GPU block start separates means within delta."""
+    ob = np.asarray(oracle_bid)
+    gb = np.asarray(gpu_bid)
+    z = np.asarray(z64, np.float64)
+    delta = delta_scale * (1.0 + float(np.abs(np.asarray(y, np.float64)).max()))
+    os_ = np.flatnonzero(np.diff(ob) != 0) + 1
+    gs = np.flatnonzero(np.diff(gb) != 0) + 1
+    if gb[0] != 0 or np.any(np.diff(gb) < 0) or np.any(np.diff(gb) > 1):
+        return False
+    gset = set(gs.tolist())
+    oset = set(os_.tolist())
+    for s in os_:
+        if abs(z[s] - z[s - 1]) > delta and s not in gset:
+            return False
+    for s in gs:
+        if s not in oset and abs(z[s] - z[s - 1]) > delta:
+            return False
+    return True
