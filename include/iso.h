@@ -1,0 +1,162 @@
+/*
+ * iso.h - C ABI of the MI355X (gfx950) batched weighted isotonic-regression
+ * library, libiso.so.
+ *
+ * The operation (paper "Merge Hulls Without Copying Vertices: GPU Isotonic
+ * Regression", section 2.1, equations (1)-(3)): for every row y[0..n) with
+ * weights w[0..n) > 0, compute the weighted least-squares non-decreasing fit
+ *
+ *     z* = argmin_{z_0 <= ... <= z_{n-1}}  sum_i w_i (z_i - y_i)^2 ,
+ *
+ * as the slope sequence of the lower convex hull of the cumulative sum diagram
+ * P_k = (W_k, S_k), W_k = sum_{i<k} w_i, S_k = sum_{i<k} w_i y_i, P_0 = (0, 0):
+ * z*_i is the slope of the hull edge above [W_i, W_{i+1}].  Rows are
+ * independent problems of one common length (paper section 3, first paragraph;
+ * rectangular batches only, section 6).
+ *
+ * Conventions shared by every entry point
+ *   - y, w, out, block_id are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), row-major and contiguous: element (r, i) is at r*n + i.  They
+ *     are caller-owned; the library never frees or retains them.
+ *   - y, w, out are float32 and must be 4-byte aligned; block_id is int32.
+ *   - w == NULL means unit weights.
+ *   - The fit is accumulated in f64 and each output value is rounded once to
+ *     float32 (round to nearest even), as the paper's section 6 ("Output")
+ *     asks.  The output is not forced to be monotone (same section).
+ *   - block_id (optional, NULL = not written): for each element, the 0-based
+ *     index of its block (hull edge) within its row; non-decreasing along the
+ *     row, +1 at every block start.  The paper's one-byte block-start flag
+ *     (section 6, "Gradient") is block_id[i] != block_id[i-1].  Where adjacent
+ *     blocks have equal means the library may split or pool them (a point on
+ *     a hull edge changes no slope, section 4, after Corollary 4.5).
+ *
+ * Errors (return value; also see iso_status_str)
+ *   ISO_OK               success.
+ *   ISO_WARN_NONFINITE   some rows hold a NaN or infinity in y: those rows'
+ *                        out is NaN and their block_id is -1; other rows are
+ *                        exact.  (The paper keeps per-row NaN flags, section 6.)
+ *   ISO_ERR_ARG          a NULL y or out, rows < 0 or n < 0, rows*n too large,
+ *                        an output overlapping an input, or bad flags.
+ *                        Nothing is launched.
+ *   ISO_ERR_WEIGHT       some w_i <= 0 or non-finite (the problem needs
+ *                        w_i > 0, section 2.1).  out is unspecified.
+ *   ISO_ERR_NOMEM        iso_fit could not allocate its cached workspace.
+ *   ISO_ERR_HIP          a HIP runtime call or kernel launch failed.
+ *   ISO_ERR_WORKSPACE    iso_fit_ex got a workspace smaller than
+ *                        iso_workspace_bytes() asks for.  Nothing launched.
+ *   rows == 0 or n == 0 is a no-op that returns ISO_OK.
+ *
+ * The two warning/error statuses that depend on the data (NONFINITE, WEIGHT)
+ * are only reported when the call checks: iso_fit always does; iso_fit_ex
+ * does unless ISO_F_NOCHECK is set (then it only enqueues work and returns
+ * ISO_OK; NaN rows still come out NaN).
+ */
+#ifndef ISO_H
+#define ISO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ISO_OK = 0,
+    ISO_WARN_NONFINITE = 1,
+    ISO_ERR_ARG = -1,
+    ISO_ERR_WEIGHT = -2,
+    ISO_ERR_NOMEM = -3,
+    ISO_ERR_HIP = -4,
+    ISO_ERR_WORKSPACE = -5
+};
+
+enum {
+    /* Enqueue only: no device-to-host wait for the data checks. */
+    ISO_F_NOCHECK = 1u,
+    /* Non-increasing fit instead: the increasing fit of -y, negated (paper
+     * section 2.1: the decreasing problem is the increasing one for -y). */
+    ISO_F_DECREASING = 2u,
+    /* Measurement control: merge the chunk hulls of long rows by copying the
+     * surviving vertices at every level of the merge tree (the paper's
+     * "grid copy" control, sections 7.3-7.4) instead of segment lists.  Same
+     * result; more memory traffic.  Needs the larger workspace that
+     * iso_workspace_bytes reports for this flag. */
+    ISO_F_COPY_CONTROL = 4u,
+    /* For iso_workspace_bytes only: size the workspace for a weighted call
+     * (w != NULL).  Ignored by the fitting calls. */
+    ISO_F_WEIGHTED_HINT = 0x100u
+};
+
+/*
+ * iso_fit - blocking fit on the null stream of the current device.
+ *   y    [rows*n] f32, device.          w   [rows*n] f32 or NULL, device.
+ *   out  [rows*n] f32, device, written.  May not overlap y or w.
+ * Uses a workspace the library allocates once per device and grows on demand
+ * (freed by iso_release).  Waits for the GPU and always runs the data checks.
+ * Not safe to call concurrently from several host threads on one device.
+ */
+int iso_fit(const float* y, const float* w, int64_t rows, int64_t n, float* out);
+
+/*
+ * iso_fit_ex - the fit on a caller stream with a caller workspace.
+ *   block_id        [rows*n] int32, device, or NULL.
+ *   workspace       device buffer of at least iso_workspace_bytes(rows, n,
+ *                   flags) bytes, 256-byte aligned; may be NULL only when
+ *                   that size is 0.  Owned by the caller; its contents need
+ *                   no initialisation and are scratch after the call.
+ *   workspace_bytes its size.
+ *   stream          a hipStream_t (NULL = the null stream).
+ *   flags           ISO_F_* bits.
+ * Without ISO_F_NOCHECK the call synchronises with `stream` to read the
+ * device's per-row data flags.  Calls that share one workspace must not
+ * overlap in time.
+ */
+int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* out,
+               int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
+               uint32_t flags);
+
+/* Bytes of device workspace iso_fit_ex needs for this shape and these flags
+ * (weighted or not is part of the shape: pass ISO_F_WEIGHTED_HINT in flags
+ * when w will be non-NULL).  Returns 0 for an empty or invalid shape. */
+size_t iso_workspace_bytes(int64_t rows, int64_t n, uint32_t flags);
+
+/* A static English description of a status code. */
+const char* iso_status_str(int status);
+
+/* Frees the workspace that iso_fit caches on each device it has used. */
+void iso_release(void);
+
+/* Chunk size (points per chunk hull) that long rows of length n use; rows
+ * with n at most iso_short_row_max() are fitted whole by one workgroup. */
+int64_t iso_chunk_size(int64_t n);
+int64_t iso_short_row_max(void);
+
+/*
+ * Measurement hooks (for benchmarks; not needed to fit).  After
+ * iso_timing_enable(1), every fitting call made from any host thread records a
+ * HIP event on its stream before each of its kernel launches and after the
+ * last, so each launch's device duration can be read.  iso_timing_read waits
+ * for the recorded events, adds each launch's duration (ms) to
+ * ms[phase] and 1 to launches[phase] for its phase (ISO_PHASE_*), for phase <
+ * nphase, clears the record and returns the number of launches read (or
+ * ISO_ERR_HIP).  Enabling adds the event records to the stream and so may
+ * widen the gaps between launches; iso_timing_enable(0) stops recording.
+ */
+enum {
+    ISO_PHASE_SHORT_ROWS = 0,  /* whole short rows in one kernel          */
+    ISO_PHASE_CHUNK_HULLS = 1, /* prefix sums, chunk hulls, chunk slots   */
+    ISO_PHASE_MERGE = 2,       /* segment-list merge tree + chunk records */
+    ISO_PHASE_EXPAND = 3,      /* slope expansion (the fit)               */
+    ISO_PHASE_COPY_BRIDGE = 4, /* copy control: bridges of one level      */
+    ISO_PHASE_COPY_MOVE = 5,   /* copy control: vertex rewrite of a level */
+    ISO_PHASE_COUNT = 6
+};
+int iso_timing_enable(int on);
+int iso_timing_read(double* ms, int64_t* launches, int nphase);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISO_H */

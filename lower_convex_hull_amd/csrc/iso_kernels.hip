@@ -1,0 +1,879 @@
+// gfx950 kernels of the batched weighted isotonic fit.
+//
+// The fit of a row is the slope sequence of the lower convex hull of its
+// cumulative sum diagram P_k = (W_k, S_k) (paper "Merge Hulls Without Copying
+// Vertices: GPU Isotonic Regression", section 2.1, equations (2)-(3)).  The
+// kernels build that hull in three levels (paper section 3):
+//
+//   thread  - the hull of its 16 consecutive points, a monotone chain whose
+//             stack is a bit mask (section 3.1);
+//   group   - the threads of a workgroup merge their hulls pairwise by walking
+//             to the bridge and clearing the bits under it (section 3.2);
+//   row     - chunk hulls, written once to the workspace, are merged up a tree
+//             whose nodes are lists of segments of chunk hulls, at most one
+//             per chunk (section 3.3, Definition 4.3, Theorem 4.4).
+//
+// and reconstruct the fit from the root list (section 3.4, Corollary 4.5).
+// Rows of at most 4096 elements are finished inside one workgroup.
+//
+// All coordinates are f64: chunk-relative inside a chunk, plus f64 chunk starts
+// from a scan of the chunk totals.  (The pages' float pairs and exponent
+// filters, section 6 "Coordinates" and appendix B, exist because their GPU ran
+// f64 at a thirty-second of the f32 rate; gfx950 runs f64 FMA at the f32 rate.)
+#include "iso_kernels.hpp"
+
+#include <math.h>
+
+namespace iso {
+namespace {
+
+struct Pt {
+    double w;
+    double s;
+};
+
+// z-component of (b - a) x (c - a).  For a, b, c in increasing abscissa, > 0
+// means b lies strictly below the chord from a to c (a strict left turn), so b
+// is a hull vertex of {a, b, c}; <= 0 means b is on or above the chord and is
+// dropped (collinear middle points are not vertices, paper section 2.1).
+__device__ __forceinline__ double cross3(Pt a, Pt b, Pt c) {
+    return (b.w - a.w) * (c.s - a.s) - (b.s - a.s) * (c.w - a.w);
+}
+
+__device__ __forceinline__ int msb32(uint32_t x) { return 31 - __clz((int)x); }
+__device__ __forceinline__ int lsb32(uint32_t x) { return __ffs((int)x) - 1; }
+
+// ----------------------------------------------------------------------------
+// Workgroup scans.
+// ----------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ double wg_excl_scan(double v, double* red, double* total) {
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    double x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        double t = __shfl_up(x, d);
+        if (lane >= d) x += t;
+    }
+    double excl = __shfl_up(x, 1);
+    if (lane == 0) excl = 0.0;
+    if (lane == 63) red[wid] = x;
+    __syncthreads();
+    double before = 0.0, all = 0.0;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) {
+        double t = red[k];
+        if (k < wid) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + excl;
+}
+
+template <int NT>
+__device__ __forceinline__ int wg_excl_scan_int(int v, int* red, int* total) {
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int t = __shfl_up(x, d);
+        if (lane >= d) x += t;
+    }
+    int excl = __shfl_up(x, 1);
+    if (lane == 0) excl = 0;
+    if (lane == 63) red[wid] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) {
+        int t = red[k];
+        if (k < wid) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + excl;
+}
+
+// ----------------------------------------------------------------------------
+// The hull of one workgroup's points.
+//
+// Thread L owns points L*P .. L*P+P of the block (P+1 points; its last point
+// is thread L+1's first).  Bits 0..P-1 of mask[L] mark which of points
+// L*P .. L*P+P-1 are vertices; the block's last point NT*P is always one.
+// ----------------------------------------------------------------------------
+template <int NT, int P, bool WT>
+struct HullSmem {
+    double S[NT * P + 1];            // block-relative S_k
+    double W[WT ? NT * P + 1 : 1];   // block-relative W_k (weighted only)
+    uint32_t mask[NT];
+    uint32_t occ[(NT + 31) / 32];    // bit L: mask[L] != 0
+    int32_t blo[NT];                 // bridge ends of the merge led by thread L
+    int32_t bhi[NT];
+    double red[NT / 64 + 1];
+    int ired[NT / 64 + 1];
+    int flag;
+};
+
+template <int NT, int P, bool WT>
+struct Block {
+    HullSmem<NT, P, WT>& sm;
+    int len;  // real elements in the block; points beyond len repeat point len
+
+    __device__ __forceinline__ Pt pt(int k) const {
+        Pt p;
+        p.s = sm.S[k];
+        p.w = WT ? sm.W[k] : (double)min(k, len);
+        return p;
+    }
+
+    // Highest vertex below point k, searching threads >= lo_lane.
+    __device__ int prev_vertex(int k, int lo_lane) const {
+        int Lk = k / P;
+        int b = k - Lk * P;
+        if (Lk < NT && b > 0) {
+            uint32_t m = sm.mask[Lk] & ((1u << b) - 1u);
+            if (m) return Lk * P + msb32(m);
+        }
+        int x = Lk - 1;
+        while (x >= lo_lane) {
+            int wi = x >> 5;
+            uint32_t word = sm.occ[wi] & ((2u << (x & 31)) - 1u);
+            if (word) {
+                int c = (wi << 5) + msb32(word);
+                if (c < lo_lane) break;
+                return c * P + msb32(sm.mask[c]);
+            }
+            x = (wi << 5) - 1;
+        }
+        return lo_lane * P;  // the group's first point is always a vertex
+    }
+
+    // Lowest vertex above point k among threads < hi_lane, else the group's
+    // last point hi_lane*P.
+    __device__ int next_vertex(int k, int hi_lane) const {
+        int Lk = k / P;
+        int b = k - Lk * P;
+        if (Lk < hi_lane) {
+            uint32_t m = sm.mask[Lk] & ~((2u << b) - 1u);
+            if (m) return Lk * P + lsb32(m);
+        }
+        int x = Lk + 1;
+        while (x < hi_lane) {
+            int wi = x >> 5;
+            uint32_t word = sm.occ[wi] & ~((1u << (x & 31)) - 1u);
+            if (word) {
+                int c = (wi << 5) + lsb32(word);
+                if (c >= hi_lane) break;
+                return c * P + lsb32(sm.mask[c]);
+            }
+            x = (wi + 1) << 5;
+        }
+        return hi_lane * P;
+    }
+};
+
+// Loads the block's elements, forms the block-relative cumulative sums, and
+// leaves in sm.mask the vertices of the block's lower hull.  Returns this
+// thread's element values (sign applied, sanitised) in yv.
+template <int NT, int P, bool WT>
+__device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
+                           const float* __restrict__ gw, int len, float sign, float (&yv)[P]) {
+    const int L = threadIdx.x;
+    const int base = L * P;
+    float wv[P];
+    int bad = 0;
+    if (threadIdx.x == 0) sm.flag = 0;
+
+    // ---- load (each thread its P consecutive elements) and check the data
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+        int e = base + b;
+        bool in = e < len;
+        float yy = in ? gy[e] : 0.0f;
+        float ww = 1.0f;
+        if (WT) ww = in ? gw[e] : 0.0f;
+        if (in) {
+            if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
+            if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
+        } else {
+            ww = 0.0f;
+        }
+        yv[b] = sign * yy;
+        wv[b] = ww;
+    }
+
+    // ---- prefix sums (paper section 2.1, equation (2)), in f64
+    double ps[P];
+    double pw[P];
+    double ls = 0.0, lw = 0.0;
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+        if (WT) {
+            ls += (double)wv[b] * (double)yv[b];  // exact product of two f32
+            lw += (double)wv[b];
+            pw[b] = lw;
+        } else {
+            ls += (double)yv[b];
+        }
+        ps[b] = ls;
+    }
+    double tot;
+    double xs = wg_excl_scan<NT>(ls, sm.red, &tot);
+    double xw = 0.0;
+    if (WT) xw = wg_excl_scan<NT>(lw, sm.red, &tot);
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+        sm.S[base + b + 1] = xs + ps[b];
+        if (WT) sm.W[base + b + 1] = xw + pw[b];
+    }
+    if (L == 0) {
+        sm.S[0] = 0.0;
+        if (WT) sm.W[0] = 0.0;
+    }
+    if (bad) atomicOr(&sm.flag, bad);
+
+    // ---- candidates: point k is a vertex only if the slope into it (the
+    // value of element k-1) is below the slope out of it (element k).  Points
+    // next to a padding element are kept as candidates; padding points
+    // (beyond len) that are not thread ends are dropped, since they repeat
+    // point len.
+    uint32_t cand = 1u | (1u << P);
+#pragma unroll
+    for (int k = 1; k < P; ++k) {
+        int pidx = base + k;
+        bool realL = pidx - 1 < len, realR = pidx < len;
+        bool c;
+        if (pidx > len) c = false;
+        else if (realL && realR) c = yv[k - 1] < yv[k];
+        else c = true;
+        if (c) cand |= 1u << k;
+    }
+    __syncthreads();
+
+    Block<NT, P, WT> B{sm, len};
+
+    // ---- thread hull: monotone chain over the candidates, the stack a bit
+    // mask (paper section 3.1).  Each pass pops or pushes; both outcomes need
+    // one LDS load, whose address is selected first.
+    const uint32_t full = (P == 31) ? 0xffffffffu : ((2u << P) - 1u);
+    uint32_t stk;
+    if (cand == full) {
+        stk = full;  // every point locally convex: the chain keeps them all
+    } else {
+        stk = 1u;
+        int t = 0, u = -1;
+        Pt T = B.pt(base), U = T;
+        uint32_t rest = cand & ~1u;
+        int c = lsb32(rest);
+        Pt Cp = B.pt(base + c);
+        for (int it = 0; it < 2 * P + 2 && c <= P; ++it) {
+            bool pop = (u >= 0) && (cross3(U, T, Cp) <= 0.0);
+            int addr;
+            if (pop) {
+                stk &= ~(1u << t);
+                t = u;
+                T = U;
+                uint32_t below = stk & ((1u << u) - 1u);
+                u = below ? msb32(below) : -1;
+                addr = u < 0 ? 0 : u;
+            } else {
+                stk |= 1u << c;
+                u = t;
+                U = T;
+                t = c;
+                T = Cp;
+                uint32_t above = cand & ~((2u << c) - 1u);
+                c = above ? lsb32(above) : P + 1;
+                addr = c > P ? P : c;
+            }
+            Pt Lp = B.pt(base + addr);
+            if (pop) U = Lp;
+            else Cp = Lp;
+        }
+    }
+    uint32_t my = stk & ((1u << P) - 1u);
+    sm.mask[L] = my;
+    {
+        unsigned long long bal = __ballot(my != 0u);
+        if ((L & 31) == 0) sm.occ[L >> 5] = (uint32_t)(bal >> (L & 32));
+    }
+    __syncthreads();
+
+    // ---- merge the thread hulls pairwise (paper section 3.2; Lemma 4.2's
+    // walk).  The first thread of each pair of groups walks to the bridge;
+    // then every thread clears its bits strictly inside the bridge.
+    for (int r = 0; (1 << r) < NT; ++r) {
+        const int g = 2 << r, half = 1 << r;
+        if ((L & (g - 1)) == 0) {
+            const int lo_lane = L, hi_lane = L + g;
+            const int s = (L + half) * P;
+            const int lo_pt = lo_lane * P, hi_pt = hi_lane * P;
+            int a = B.prev_vertex(s, lo_lane);
+            int b = B.next_vertex(s, hi_lane);
+            Pt Pa = B.pt(a), Ps = B.pt(s), Pb = B.pt(b);
+            if (cross3(Pa, Ps, Pb) > 0.0) {
+                a = s;
+                b = s;  // convex at s: nothing removed
+            } else {
+                // walk: a moves left while its turn towards b is not strictly
+                // left, b moves right likewise, until neither moves.  Every
+                // move removes a vertex, so the walk ends; the cap only guards.
+                for (int pass = 0; pass < 2 * NT * P + 4; ++pass) {
+                    bool moved = false;
+                    while (a > lo_pt) {
+                        int a2 = B.prev_vertex(a, lo_lane);
+                        Pt P2 = B.pt(a2);
+                        if (cross3(P2, Pa, Pb) <= 0.0) { a = a2; Pa = P2; moved = true; }
+                        else break;
+                    }
+                    while (b < hi_pt) {
+                        int b2 = B.next_vertex(b, hi_lane);
+                        Pt P2 = B.pt(b2);
+                        if (cross3(Pa, Pb, P2) <= 0.0) { b = b2; Pb = P2; moved = true; }
+                        else break;
+                    }
+                    if (!moved) break;
+                }
+            }
+            sm.blo[L] = a;
+            sm.bhi[L] = b;
+        }
+        __syncthreads();
+        {
+            const int ldr = L & ~(g - 1);
+            const int a = sm.blo[ldr], b = sm.bhi[ldr];
+            int k0 = max(a + 1, base), k1 = min(b - 1, base + P - 1);
+            if (k0 <= k1) {
+                uint32_t clr = ((k1 - base == 31) ? 0xffffffffu : ((2u << (k1 - base)) - 1u)) &
+                               ~((1u << (k0 - base)) - 1u);
+                my &= ~clr;
+                sm.mask[L] = my;
+            }
+            unsigned long long bal = __ballot(my != 0u);
+            if ((L & 31) == 0) sm.occ[L >> 5] = (uint32_t)(bal >> (L & 32));
+        }
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Short rows: the whole row in one workgroup, fit written directly.
+// ----------------------------------------------------------------------------
+template <int NT, int P, bool WT>
+__global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
+                                                   const float* __restrict__ w, int64_t n,
+                                                   float sign, float* __restrict__ out,
+                                                   int32_t* __restrict__ block_id,
+                                                   int32_t* __restrict__ row_flag) {
+    __shared__ HullSmem<NT, P, WT> sm;
+    const int64_t row = blockIdx.x;
+    const float* gy = y + row * n;
+    const float* gw = WT ? w + row * n : nullptr;
+    const int len = (int)n;
+    float yv[P];
+    block_hull<NT, P, WT>(sm, gy, gw, len, sign, yv);
+
+    const int L = threadIdx.x;
+    const int base = L * P;
+    const uint32_t my = sm.mask[L];
+    const int flag = sm.flag;
+    if (L == 0) row_flag[row] = flag;
+    float* go = out + row * n;
+    int32_t* gb = block_id ? block_id + row * n : nullptr;
+    if (flag & kFlagNonfinite) {
+        for (int b = 0; b < P; ++b) {
+            int e = base + b;
+            if (e < len) {
+                go[e] = __builtin_nanf("");
+                if (gb) gb[e] = -1;
+            }
+        }
+        return;
+    }
+    // vertex before this thread's points (max-scan from the left) and the first
+    // vertex after them (min-scan from the right); vertex count before them.
+    int lastv = my ? base + msb32(my) : -1;
+    int firstv = my ? base + lsb32(my) : NT * P;
+    int cnt = __popc(my);
+    __shared__ int s_last[NT];
+    __shared__ int s_first[NT];
+    s_last[L] = lastv;
+    s_first[L] = firstv;
+    int total;
+    int before = wg_excl_scan_int<NT>(cnt, sm.ired, &total);  // contains a barrier
+    int prev_in = -1;
+    int next_in = NT * P;
+    for (int k = L - 1; k >= 0; --k) {
+        int v = s_last[k];
+        if (v >= 0) { prev_in = v; break; }
+    }
+    for (int k = L + 1; k < NT; ++k) {
+        int v = s_first[k];
+        if (v < NT * P) { next_in = v; break; }
+    }
+    Block<NT, P, WT> B{sm, len};
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+        int e = base + b;
+        if (e >= len) break;
+        uint32_t upto = (b == 31) ? 0xffffffffu : ((2u << b) - 1u);
+        uint32_t below = my & upto;
+        uint32_t above = my & ~upto;
+        int pv = below ? base + msb32(below) : prev_in;
+        int nv = above ? base + lsb32(above) : next_in;
+        float val;
+        if (pv == e && nv == e + 1) {
+            val = yv[b];  // both ends are vertices: the edge is the element itself
+        } else {
+            Pt A = B.pt(pv), C = B.pt(nv);
+            val = (float)((C.s - A.s) / (C.w - A.w));
+        }
+        go[e] = sign * val;
+        if (gb) gb[e] = before + __popc(below) - 1;  // point 0 is always a vertex
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Long rows, phase 1: one workgroup per chunk builds the chunk's hull and
+// writes it once to its slot (paper section 3.3), with the chunk's totals.
+// ----------------------------------------------------------------------------
+template <bool WT>
+__global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict__ y,
+                                                         const float* __restrict__ w, int64_t n,
+                                                         int m, float sign, LongWs ws) {
+    constexpr int NT = kLongNT, P = kLongP, C = kChunk;
+    __shared__ HullSmem<NT, P, WT> sm;
+    const int64_t gid = blockIdx.x;  // row * m + chunk
+    const int64_t row = gid / m;
+    const int j = (int)(gid - row * m);
+    const int64_t off = row * n + (int64_t)j * C;
+    const int len = (int)min((int64_t)C, n - (int64_t)j * C);
+    float yv[P];
+    block_hull<NT, P, WT>(sm, y + off, WT ? w + off : nullptr, len, sign, yv);
+
+    const int L = threadIdx.x;
+    const int base = L * P;
+    const uint32_t my = sm.mask[L];
+    int total;
+    int rank = wg_excl_scan_int<NT>(__popc(my), sm.ired, &total);
+    const size_t slot = (size_t)gid * (C + 1);
+    uint32_t bits = my;
+    while (bits) {
+        int b = lsb32(bits);
+        bits &= bits - 1u;
+        int k = base + b;
+        ws.slot_idx[slot + rank] = (uint16_t)min(k, len);
+        ws.slot_S[slot + rank] = sm.S[k];
+        if (WT) ws.slot_W[slot + rank] = sm.W[k];
+        ++rank;
+    }
+    if (L == NT - 1) {
+        // the chunk's last point (point len; padding repeats it) ends the hull
+        ws.slot_idx[slot + total] = (uint16_t)len;
+        ws.slot_S[slot + total] = sm.S[C];
+        if (WT) ws.slot_W[slot + total] = sm.W[C];
+        ws.hull_cnt[gid] = total + 1;
+        ws.tot_S[gid] = sm.S[C];
+        if (WT) ws.tot_W[gid] = sm.W[C];
+        ws.chunk_flag[gid] = sm.flag;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Long rows, phase 2: the merge tree over segment lists (paper section 3.3,
+// Algorithm 1, Definition 4.3, Theorem 4.4), one workgroup per row, a thread
+// per merge, every level in one launch.  Then the per-chunk reconstruction
+// records (section 3.4, Corollary 4.5).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int dchunk(uint2 d) { return (int)d.x; }
+__device__ __forceinline__ int dlo(uint2 d) { return (int)(d.y & 0xffffu); }
+__device__ __forceinline__ int dhi(uint2 d) { return (int)(d.y >> 16); }
+__device__ __forceinline__ uint2 mkdesc(int j, int lo, int hi) {
+    return make_uint2((uint32_t)j, (uint32_t)lo | ((uint32_t)hi << 16));
+}
+
+struct Cur {
+    int seg;
+    int pos;
+};
+
+struct RowView {
+    const uint16_t* idx;
+    const double* S;
+    const double* W;
+    const double* stS;
+    const double* stW;
+    bool weighted;
+
+    // Vertex `pos` of chunk j's slot, in coordinates relative to chunk jr's
+    // start: the chunk-start difference first, then the chunk-relative part.
+    __device__ __forceinline__ Pt vtx(int j, int pos, int jr) const {
+        size_t o = (size_t)j * (kChunk + 1) + pos;
+        Pt p;
+        p.s = (stS[j] - stS[jr]) + S[o];
+        if (weighted) p.w = (stW[j] - stW[jr]) + W[o];
+        else p.w = (double)((int64_t)(j - jr) * kChunk + (int64_t)idx[o]);
+        return p;
+    }
+};
+
+struct List {
+    uint2* d;
+    int n;
+    __device__ __forceinline__ Cur first() const { return Cur{0, dlo(d[0])}; }
+    __device__ __forceinline__ Cur last() const { return Cur{n - 1, dhi(d[n - 1])}; }
+    __device__ __forceinline__ bool is_first(Cur c) const { return c.seg == 0 && c.pos == dlo(d[0]); }
+    __device__ __forceinline__ bool is_last(Cur c) const {
+        return c.seg == n - 1 && c.pos == dhi(d[n - 1]);
+    }
+    __device__ __forceinline__ Cur prev(Cur c) const {
+        return c.pos > dlo(d[c.seg]) ? Cur{c.seg, c.pos - 1} : Cur{c.seg - 1, dhi(d[c.seg - 1])};
+    }
+    __device__ __forceinline__ Cur next(Cur c) const {
+        return c.pos < dhi(d[c.seg]) ? Cur{c.seg, c.pos + 1} : Cur{c.seg + 1, dlo(d[c.seg + 1])};
+    }
+    __device__ __forceinline__ Pt pt(const RowView& X, Cur c, int jr) const {
+        return X.vtx(dchunk(d[c.seg]), c.pos, jr);
+    }
+};
+
+// First vertex of the list range [X, Y] that satisfies a predicate which is
+// false then true along the range and true at Y: bisection over segments (by
+// each segment's last in-range vertex), then within one segment.
+template <class F>
+__device__ Cur find_first(const List& Lst, Cur X, Cur Y, F pred) {
+    int lo = X.seg, hi = Y.seg;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        Cur c{mid, mid == Y.seg ? Y.pos : dhi(Lst.d[mid])};
+        if (pred(c)) hi = mid;
+        else lo = mid + 1;
+    }
+    int plo = (lo == X.seg) ? X.pos : dlo(Lst.d[lo]);
+    int phi = (lo == Y.seg) ? Y.pos : dhi(Lst.d[lo]);
+    while (plo < phi) {
+        int mid = (plo + phi) >> 1;
+        if (pred(Cur{lo, mid})) phi = mid;
+        else plo = mid + 1;
+    }
+    return Cur{lo, plo};
+}
+
+// Merges the lists stored from slots a and b (b = a + span), writing the result
+// from slot a (Algorithm 1).
+__device__ void merge_lists(const RowView& X, uint2* desc, int32_t* cnt, int a, int b) {
+    List Lq{desc + a, cnt[a]};
+    List Rq{desc + b, cnt[b]};
+    const int jr = b;  // chunk of the shared point s
+    Cur sL = Lq.last();
+    Cur sR = Rq.first();
+    Pt Ps = Rq.pt(X, sR, jr);
+    Cur A = Lq.prev(sL);  // every node has at least its two end points
+    Cur B = Rq.next(sR);
+    Pt PA = Lq.pt(X, A, jr), PB = Rq.pt(X, B, jr);
+    if (cross3(PA, Ps, PB) > 0.0) {
+        A = sL;  // convex at s: keep s once, in L
+    } else {
+        // walk (Lemma 4.2), at most kWalkCap steps
+        int steps = 0;
+        bool done = false;
+        for (;;) {
+            bool moved = false;
+            while (!Lq.is_first(A) && steps < kWalkCap) {
+                Cur A2 = Lq.prev(A);
+                Pt P2 = Lq.pt(X, A2, jr);
+                if (cross3(P2, PA, PB) <= 0.0) { A = A2; PA = P2; moved = true; ++steps; }
+                else break;
+            }
+            while (!Rq.is_last(B) && steps < kWalkCap) {
+                Cur B2 = Rq.next(B);
+                Pt P2 = Rq.pt(X, B2, jr);
+                if (cross3(PA, PB, P2) <= 0.0) { B = B2; PB = P2; moved = true; ++steps; }
+                else break;
+            }
+            if (!moved) { done = true; break; }
+            if (steps >= kWalkCap) break;
+        }
+        if (!done) {
+            // nested bisection (paper section 3.3, Theorem 5.2): a is the first
+            // vertex of L on whose tangent line to R its successor does not lie
+            // below; b is where that tangent touches R.
+            const Cur A0 = Lq.prev(sL);
+            const Cur B0 = Rq.next(sR);
+            const Cur RL = Rq.last();
+            auto tangent = [&](Pt Pa) -> Cur {
+                return find_first(Rq, B0, RL, [&](Cur r) -> bool {
+                    if (Rq.is_last(r)) return true;
+                    Pt Pr = Rq.pt(X, r, jr);
+                    Pt Pn = Rq.pt(X, Rq.next(r), jr);
+                    return cross3(Pa, Pr, Pn) > 0.0;
+                });
+            };
+            A = find_first(Lq, Lq.first(), A0, [&](Cur c) -> bool {
+                if (c.seg == A0.seg && c.pos == A0.pos) return true;
+                Pt Pc = Lq.pt(X, c, jr);
+                Cur t = tangent(Pc);
+                Pt Pt_ = Rq.pt(X, t, jr);
+                Pt Pn = Lq.pt(X, Lq.next(c), jr);
+                return cross3(Pc, Pt_, Pn) >= 0.0;
+            });
+            B = tangent(Lq.pt(X, A, jr));
+        }
+    }
+    // cut L after A, R before B, move R's tail to follow L's list
+    uint2 dl = Lq.d[A.seg];
+    Lq.d[A.seg] = mkdesc(dchunk(dl), dlo(dl), A.pos);
+    uint2 dr = Rq.d[B.seg];
+    Rq.d[B.seg] = mkdesc(dchunk(dr), B.pos, dhi(dr));
+    const int nl = A.seg + 1;
+    const int nr = Rq.n - B.seg;
+    for (int i = 0; i < nr; ++i) Lq.d[nl + i] = Rq.d[B.seg + i];
+    cnt[a] = nl + nr;
+}
+
+template <bool WT>
+__global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
+    constexpr int NT = kMergeNT;
+    __shared__ double red[NT / 64 + 1];
+    __shared__ int ired[NT / 64 + 1];
+    __shared__ int sflag;
+    const int64_t row = blockIdx.x;
+    const int64_t rb = row * m;
+    const int tid = threadIdx.x;
+
+    // ---- row flags, chunk starts (exclusive scan of the chunk totals)
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int f = 0;
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    if (f) atomicOr(&sflag, f);
+    double carryS = 0.0, carryW = 0.0;
+    for (int t0 = 0; t0 < m; t0 += NT) {
+        int j = t0 + tid;
+        double vs = j < m ? ws.tot_S[rb + j] : 0.0;
+        double tot;
+        double xs = wg_excl_scan<NT>(vs, red, &tot);
+        if (j < m) ws.st_S[rb + j] = carryS + xs;
+        carryS += tot;
+        if (WT) {
+            double vw = j < m ? ws.tot_W[rb + j] : 0.0;
+            double xw = wg_excl_scan<NT>(vw, red, &tot);
+            if (j < m) ws.st_W[rb + j] = carryW + xw;
+            carryW += tot;
+        }
+    }
+    for (int j = tid; j < m; j += NT) {
+        ws.desc[rb + j] = mkdesc(j, 0, ws.hull_cnt[rb + j] - 1);
+        ws.node_cnt[rb + j] = 1;
+    }
+    __syncthreads();
+    if (tid == 0) ws.row_flag[row] = sflag;
+
+    RowView X{ws.slot_idx + rb * (kChunk + 1), ws.slot_S + rb * (kChunk + 1),
+              WT ? ws.slot_W + rb * (kChunk + 1) : nullptr, ws.st_S + rb,
+              WT ? ws.st_W + rb : nullptr, WT};
+    uint2* desc = ws.desc + rb;
+    int32_t* cnt = ws.node_cnt + rb;
+
+    // ---- the merge tree, level by level
+    for (int span = 1; span < m; span <<= 1) {
+        const int nm = (m - span + 2 * span - 1) / (2 * span);
+        for (int k = tid; k < nm; k += NT) merge_lists(X, desc, cnt, 2 * k * span, 2 * k * span + span);
+        __syncthreads();
+    }
+
+    // ---- reconstruction records (Corollary 4.5)
+    const int nroot = cnt[0];
+    int carry = 0;
+    int32_t* vb = ws.vb + rb;
+    for (int t0 = 0; t0 < nroot; t0 += NT) {
+        int i = t0 + tid;
+        int v = 0;
+        if (i < nroot) {
+            uint2 d = desc[i];
+            v = dhi(d) - dlo(d) + 1;
+        }
+        int tot;
+        int x = wg_excl_scan_int<NT>(v, ired, &tot);
+        if (i < nroot) vb[i] = carry + x;
+        carry += tot;
+    }
+    __syncthreads();
+    for (int j = tid; j < m; j += NT) {
+        // first root descriptor whose chunk is >= j
+        int lo = 0, hi = nroot - 1;
+        while (lo < hi) {
+            int mid = (lo + hi) >> 1;
+            if (dchunk(desc[mid]) >= j) hi = mid;
+            else lo = mid + 1;
+        }
+        const int i = lo;
+        const uint2 d = desc[i];
+        ChunkRec rc;
+        rc.pad = 0;
+        rc.vb = vb[i];
+        if (dchunk(d) == j) {
+            rc.lo = dlo(d);
+            rc.hi = dhi(d);
+            rc.slope_in = 0.0;
+            rc.slope_out = 0.0;
+            if (i > 0) {
+                uint2 p = desc[i - 1];
+                Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
+                rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+            }
+            if (i + 1 < nroot) {
+                uint2 q = desc[i + 1];
+                Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
+                rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
+            }
+        } else {
+            // the chunk lies under one edge, from the last vertex of the
+            // previous segment to the first vertex of the next (i >= 1: chunk 0
+            // always holds the row's first point)
+            uint2 p = desc[i - 1];
+            Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
+            rc.lo = -1;
+            rc.hi = -1;
+            rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+            rc.slope_out = rc.slope_in;
+        }
+        ws.rec[rb + j] = rc;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Long rows, phase 3: every element takes the slope of the row-hull edge above
+// it (paper equation (3), section 3.4).
+// ----------------------------------------------------------------------------
+template <bool WT>
+__global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
+                                                    float* __restrict__ out,
+                                                    int32_t* __restrict__ block_id) {
+    constexpr int NT = kLongNT, P = kLongP, C = kChunk;
+    __shared__ int vidx[C + 1];
+    __shared__ float vslope[C + 1];
+    const int64_t gid = blockIdx.x;
+    const int64_t row = gid / m;
+    const int j = (int)(gid - row * m);
+    const int64_t off = row * n + (int64_t)j * C;
+    const int len = (int)min((int64_t)C, n - (int64_t)j * C);
+    float* go = out + off;
+    int32_t* gb = block_id ? block_id + off : nullptr;
+    const int tid = threadIdx.x;
+    const int e0 = tid * P;
+    if (ws.row_flag[row] & kFlagNonfinite) {
+        for (int b = 0; b < P; ++b) {
+            int e = e0 + b;
+            if (e < len) {
+                go[e] = __builtin_nanf("");
+                if (gb) gb[e] = -1;
+            }
+        }
+        return;
+    }
+    const ChunkRec rc = ws.rec[gid];
+    if (rc.lo < 0) {
+        const float v = sign * (float)rc.slope_in;
+        for (int b = 0; b < P; ++b) {
+            int e = e0 + b;
+            if (e < len) {
+                go[e] = v;
+                if (gb) gb[e] = rc.vb - 1;
+            }
+        }
+        return;
+    }
+    const int nv = rc.hi - rc.lo + 1;
+    const size_t slot = (size_t)gid * (C + 1) + rc.lo;
+    for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
+    for (int v = tid; v + 1 < nv; v += NT) {
+        double ds = ws.slot_S[slot + v + 1] - ws.slot_S[slot + v];
+        double dw = WT ? ws.slot_W[slot + v + 1] - ws.slot_W[slot + v]
+                       : (double)((int)ws.slot_idx[slot + v + 1] - (int)ws.slot_idx[slot + v]);
+        vslope[v] = (float)(ds / dw);
+    }
+    __syncthreads();
+    if (e0 >= len) return;
+    // q = number of the chunk's surviving vertices at or before e0
+    int lo = 0, hi = nv;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (vidx[mid] <= e0) lo = mid + 1;
+        else hi = mid;
+    }
+    int q = lo;
+    const float sin_ = (float)rc.slope_in, sout = (float)rc.slope_out;
+    for (int b = 0; b < P; ++b) {
+        int e = e0 + b;
+        if (e >= len) break;
+        while (q < nv && vidx[q] <= e) ++q;
+        float v = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
+        go[e] = sign * v;
+        if (gb) gb[e] = rc.vb + q - 1;
+    }
+}
+
+template <int NT, int P>
+hipError_t launch_short_t(const float* y, const float* w, int64_t rows, int64_t n, float sign,
+                          float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {
+    timed_begin(0, st);
+    if (w)
+        hipLaunchKernelGGL((k_short_rows<NT, P, true>), dim3((unsigned)rows), dim3(NT), 0, st, y, w,
+                           n, sign, out, block_id, row_flag);
+    else
+        hipLaunchKernelGGL((k_short_rows<NT, P, false>), dim3((unsigned)rows), dim3(NT), 0, st, y,
+                           w, n, sign, out, block_id, row_flag);
+    timed_end(st);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
+                        float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {
+    if (n <= 64) return launch_short_t<64, 1>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    if (n <= 128) return launch_short_t<64, 2>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    if (n <= 256) return launch_short_t<64, 4>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    if (n <= 512) return launch_short_t<64, 8>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    if (n <= 1024) return launch_short_t<64, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    return launch_short_t<256, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
+}
+
+hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
+                       float* out, int32_t* block_id, bool copy_control, hipStream_t st) {
+    (void)copy_control;
+    const unsigned nblk = (unsigned)(sh.rows * sh.m);
+    const bool wt = sh.weighted;
+    timed_begin(1, st);
+    if (wt)
+        hipLaunchKernelGGL(k_chunk_hulls<true>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+                           sh.sign, ws);
+    else
+        hipLaunchKernelGGL(k_chunk_hulls<false>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+                           sh.sign, ws);
+    timed_end(st);
+    timed_begin(2, st);
+    if (wt)
+        hipLaunchKernelGGL(k_merge_rows<true>, dim3((unsigned)sh.rows), dim3(kMergeNT), 0, st, sh.m,
+                           ws);
+    else
+        hipLaunchKernelGGL(k_merge_rows<false>, dim3((unsigned)sh.rows), dim3(kMergeNT), 0, st,
+                           sh.m, ws);
+    timed_end(st);
+    timed_begin(3, st);
+    if (wt)
+        hipLaunchKernelGGL(k_expand<true>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign, ws,
+                           out, block_id);
+    else
+        hipLaunchKernelGGL(k_expand<false>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign,
+                           ws, out, block_id);
+    timed_end(st);
+    return hipGetLastError();
+}
+
+}  // namespace iso

@@ -1,0 +1,88 @@
+// Internal interface between the C ABI (iso_api.hip) and the gfx950 kernels
+// (iso_kernels.hip).  Not installed; nothing outside libiso.so includes it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace iso {
+
+// Long rows are cut into chunks of kChunk points, one 256-thread workgroup
+// each (16 points per thread).  Rows up to kShortMax elements are fitted whole
+// by one workgroup and never touch the workspace.
+constexpr int kLongNT = 256;
+constexpr int kLongP = 16;
+constexpr int kChunk = kLongNT * kLongP;  // 4096
+constexpr int kShortMax = 4096;
+constexpr int kMergeNT = 256;
+constexpr int kWalkCap = 64;  // walk steps before the merge switches to bisection
+
+// Per-row data flags written by the kernels (read back by the checking path).
+constexpr int kFlagNonfinite = 1;
+constexpr int kFlagWeight = 2;
+
+// Reconstruction record of one chunk, written by the merge phase.
+//   lo < 0: no vertex of the row's hull lies in the chunk; every element of
+//           the chunk lies under one edge of slope `slope_in`.
+//   else:   the chunk's surviving hull vertices are its slot positions lo..hi;
+//           slope_in is the edge into lo, slope_out the edge out of hi.
+//   vb:     number of row-hull vertices in earlier chunks' segments (for the
+//           block ids).
+struct ChunkRec {
+    int32_t lo;
+    int32_t hi;
+    int32_t vb;
+    int32_t pad;
+    double slope_in;
+    double slope_out;
+};
+
+// Device pointers of the long-row workspace (see plan_long in iso_api.hip).
+struct LongWs {
+    int32_t* chunk_flag;  // [R*m]
+    double* tot_S;        // [R*m] chunk totals
+    double* tot_W;        // [R*m] (weighted only)
+    int32_t* hull_cnt;    // [R*m] vertices in each chunk hull
+    uint16_t* slot_idx;   // [R*m*(C+1)] chunk-relative point index of each vertex
+    double* slot_S;       // [R*m*(C+1)] chunk-relative S of each vertex
+    double* slot_W;       // [R*m*(C+1)] chunk-relative W (weighted only)
+    double* st_S;         // [R*m] chunk starts (exclusive scan of totals)
+    double* st_W;         // [R*m] (weighted only)
+    uint2* desc;          // [R*m] segment descriptors (chunk, lo | hi << 16)
+    int32_t* node_cnt;    // [R*m] segments in the list stored from this slot
+    int32_t* vb;          // [R*m] scratch: vertex prefix over the root list
+    ChunkRec* rec;        // [R*m]
+    int32_t* row_flag;    // [R]
+    // grid-copy control only
+    uint4* cp_a;          // [R*m*(C+1)] flat vertex buffers (ping)
+    uint4* cp_b;          // (pong)
+    int32_t* cp_off;      // [R*m] node offsets (ping)
+    int32_t* cp_cnt;      // [R*m] node vertex counts (ping)
+    int32_t* cp_off2;     // [R*m] (pong)
+    int32_t* cp_cnt2;     // [R*m]
+    int32_t* cp_cut;      // [R*m] per merge: kept prefix of L (count) and start of R
+    int32_t* cp_cut2;     // [R*m]
+};
+
+struct LongShape {
+    int64_t rows;
+    int64_t n;
+    int m;         // chunks per row
+    bool weighted;
+    float sign;    // +1 increasing, -1 decreasing
+};
+
+// Launch timing for benchmarks (iso_timing_enable / iso_timing_read): when
+// enabled, timed_begin records an event before a launch and timed_end one
+// after it, on the launch's stream.
+void timed_begin(int phase, hipStream_t st);
+void timed_end(hipStream_t st);
+
+hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
+                        float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
+
+hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
+                       float* out, int32_t* block_id, bool copy_control, hipStream_t st);
+
+}  // namespace iso

@@ -1,0 +1,261 @@
+"""GPU parity: libiso.so (through its C ABI) against the CPU oracle, element by
+element, on seeded inputs.
+
+Rule (per row): max |out - z| <= 1e-5 (1 + max|y|) and the weighted objective
+within 1e-9 relative of the oracle's (tests/fitcheck.parity).  Block ids: every
+oracle block start between means that differ by more than 1e-6 (1 + max|y|) is
+a GPU block start, and every extra GPU start separates means within that.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lower_convex_hull_amd import inputs, iso
+from tests import fitcheck
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    iso.lib()
+    return t
+
+
+def gpu_fit(torch, y, w=None, flags=0, block_ids=True):
+    yt = torch.from_numpy(np.ascontiguousarray(y, np.float32)).cuda()
+    wt = None if w is None else torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    rows, n = yt.shape
+    out = torch.empty_like(yt)
+    bid = torch.empty((rows, n), dtype=torch.int32, device="cuda") if block_ids else None
+    ws = iso.workspace(rows, n, wt is not None, flags)
+    st = iso.iso_fit_ex(yt.data_ptr(), None if wt is None else wt.data_ptr(), rows, n,
+                        out.data_ptr(), None if bid is None else bid.data_ptr(), ws.data_ptr(),
+                        ws.numel(), iso._stream_handle(None), flags)
+    torch.cuda.synchronize()
+    return st, out.cpu().numpy(), (None if bid is None else bid.cpu().numpy())
+
+
+def check(torch, y, w=None, flags=0, name="", block_ids=True):
+    y = np.atleast_2d(np.asarray(y, np.float32))
+    if w is not None:
+        w = np.asarray(w, np.float32).reshape(y.shape)
+    say(f"[parity] {name} rows={y.shape[0]} n={y.shape[1]} weighted={w is not None} flags={flags}")
+    st, out, bid = gpu_fit(torch, y, w, flags, block_ids)
+    assert st == iso.ISO_OK, iso.iso_status_str(st)
+    ysign = -y if flags & iso.ISO_F_DECREASING else y
+    _, z64, obid = oracle.fit_rows_f32(ysign, w)
+    if flags & iso.ISO_F_DECREASING:
+        z64 = -z64
+    ok, wa, wo, row = fitcheck.parity(y, w, out, z64)
+    assert ok, f"{name}: abs ratio {wa:.3g}, objective ratio {wo:.3g}, row {row}"
+    if block_ids:
+        for r in range(y.shape[0]):
+            assert fitcheck.block_ids_consistent(obid[r], bid[r], z64[r], y[r]), f"{name}: block ids row {r}"
+    return out, bid, z64
+
+
+# --------------------------------------------------------------------------- pages' examples
+
+def test_worked_examples(torch):
+    for c in fitcheck.read_cases("worked_examples.txt"):
+        y = np.array([[float(v) for v in c["y"]]], np.float32)
+        want = np.array([float(v) for v in c["z"]])
+        st, out, bid = gpu_fit(torch, y)
+        assert st == 0
+        assert np.allclose(out[0], want, rtol=0, atol=1e-6), c["case"]
+
+
+def test_tiny_rows_against_brute_force(torch):
+    rng = np.random.default_rng(31)
+    for n in range(1, 13):
+        for wk in ("none", "uniform", "exp"):
+            rows = 64
+            y = rng.integers(-3, 4, (rows, n)).astype(np.float32)
+            y[rows // 2:] = rng.normal(0, 1, (rows - rows // 2, n)).astype(np.float32)
+            w = None if wk == "none" else (
+                (0.1 + rng.random((rows, n))) if wk == "uniform" else np.exp(8 * rng.random((rows, n)))
+            ).astype(np.float32)
+            st, out, _ = gpu_fit(torch, y, w)
+            assert st == 0
+            for r in range(rows):
+                zb, _ = oracle.brute_force(y[r].astype(np.float64),
+                                           None if w is None else w[r].astype(np.float64))
+                tol = 1e-5 * (1 + np.abs(y[r]).max())
+                assert np.abs(out[r] - zb).max() <= tol, (n, wk, r)
+
+
+# --------------------------------------------------------------------------- the five workloads
+
+def test_c1_row4096(torch):
+    y, w = inputs.config("c1_row4096_noisy")
+    check(torch, y, w, name="c1")
+
+
+def test_c2_batch1024x1024(torch):
+    y, w = inputs.config("c2_batch1024x1024_noisy")
+    check(torch, y, w, name="c2")
+
+
+def test_c3_row1e7_noisy(torch):
+    y, w = inputs.config("c3_row1e7_noisy")
+    check(torch, y, w, name="c3", block_ids=True)
+
+
+def test_c4_row1e7_dense(torch):
+    y, w = inputs.config("c4_row1e7_dense")
+    out, bid, _ = check(torch, y, w, name="c4")
+    # closed form: a strictly increasing row is its own fit, every element a block
+    assert np.array_equal(out[0], y[0])
+    assert np.array_equal(bid[0], np.arange(y.shape[1], dtype=np.int32))
+
+
+def test_c5_calibration_rows(torch):
+    # 16 of the 256 rows at full length (2^20), same recipe; the full batch runs
+    # in test_c5_full_batch_sampled.
+    y, w = inputs.config("c5_calib256x2p20", rows=16)
+    check(torch, y, w, name="c5x16")
+
+
+def test_c5_full_batch_sampled(torch):
+    y, w = inputs.config("c5_calib256x2p20")
+    say("[parity] c5 full batch 256 x 2^20 (oracle on 24 sampled rows)")
+    st, out, bid = gpu_fit(torch, y, w, block_ids=False)
+    assert st == 0
+    rows = np.random.default_rng(0).choice(y.shape[0], 24, replace=False)
+    _, z64, _ = oracle.fit_rows_f32(y[rows], w[rows])
+    ok, wa, wo, r = fitcheck.parity(y[rows], w[rows], out[rows], z64)
+    assert ok, (wa, wo, rows[r])
+    # every row: the output is within [min y, max y] and its KKT total is ~0
+    assert np.all(out >= 0) and np.all(out <= 1)
+
+
+# --------------------------------------------------------------------------- families, sizes, edges
+
+@pytest.mark.parametrize("n", [1000, 4096, 4097, 5000, 12289, 100_003])
+@pytest.mark.parametrize("fam", inputs.FAMILIES)
+def test_families(torch, fam, n):
+    for k, wk in enumerate(inputs.WEIGHTINGS):
+        y = inputs.family(fam, n, 1000 + k)
+        w = inputs.weights(wk, n, 1000 + k)
+        check(torch, y[None, :], w, name=f"{fam}/{wk}/{n}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 8192, 8193])
+def test_ragged_sizes(torch, n):
+    rows = 3
+    y, _ = inputs.noisy(rows, n, 40 + n)
+    w = inputs.weights("uniform", rows * n, 40 + n).reshape(rows, n)
+    check(torch, y, None, name=f"ragged/{n}")
+    check(torch, y, w, name=f"ragged-w/{n}")
+
+
+def test_batch_of_long_rows(torch):
+    y, w = inputs.calibration(6, 20_000, 77)
+    check(torch, y, w, name="long-batch")
+    y2, _ = inputs.noisy(5, 50_000, 78)
+    check(torch, y2, None, name="long-batch-noisy")
+
+
+def test_decreasing_flag(torch):
+    y, _ = inputs.noisy(4, 3000, 9)
+    check(torch, y[:, ::-1].copy(), None, flags=iso.ISO_F_DECREASING, name="dec-short")
+    y, _ = inputs.noisy(2, 30000, 10)
+    check(torch, y[:, ::-1].copy(), None, flags=iso.ISO_F_DECREASING, name="dec-long")
+
+
+def test_consecutive_floats_are_fixed_points(torch):
+    for n in (3000, 200_000):
+        y = inputs.consecutive_floats(n)[None, :]
+        say(f"[parity] consecutive floats n={n}")
+        st, out, bid = gpu_fit(torch, y)
+        assert st == 0
+        assert np.array_equal(out, y)
+        assert np.array_equal(bid[0], np.arange(n, dtype=np.int32))
+
+
+def test_cancellation_family_stress(torch):
+    # a stress test, not a gate: B up to 1e6 (paper section 7.6 goes further)
+    for big in (1e3, 1e6):
+        y = inputs.cancellation(20_000, big, 5)[None, :]
+        check(torch, y, None, name=f"cancellation/{big:g}", block_ids=False)
+
+
+def test_constant_and_decreasing_rows(torch):
+    n = 9000
+    y = np.full((2, n), 0.25, np.float32)
+    st, out, bid = gpu_fit(torch, y)
+    assert st == 0 and np.all(out == 0.25)
+    y = -np.sort(np.random.default_rng(3).random((2, n)), axis=1).astype(np.float32)
+    check(torch, y, None, name="strictly-decreasing")
+
+
+def test_nonfinite_rows_and_bad_weights(torch):
+    y, _ = inputs.noisy(4, 5000, 12)
+    y[1, 17] = np.nan
+    y[3, 4999] = np.inf
+    st, out, bid = gpu_fit(torch, y)
+    assert st == iso.ISO_WARN_NONFINITE
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
+    assert np.all(bid[1] == -1) and np.all(bid[3] == -1)
+    _, z64, _ = oracle.fit_rows_f32(y[[0, 2]])
+    assert fitcheck.parity(y[[0, 2]], None, out[[0, 2]], z64)[0]
+    ys, _ = inputs.noisy(3, 500, 13)
+    ys[2, 0] = -np.inf
+    st, out, bid = gpu_fit(torch, ys)
+    assert st == iso.ISO_WARN_NONFINITE and np.all(np.isnan(out[2])) and not np.isnan(out[:2]).any()
+    for n in (500, 5000):
+        y, _ = inputs.noisy(2, n, 14)
+        w = np.ones_like(y)
+        w[1, 3] = 0.0
+        st, _, _ = gpu_fit(torch, y, w)
+        assert st == iso.ISO_ERR_WEIGHT
+        w[1, 3] = -1.0
+        st, _, _ = gpu_fit(torch, y, w)
+        assert st == iso.ISO_ERR_WEIGHT
+        w[1, 3] = np.nan
+        st, _, _ = gpu_fit(torch, y, w)
+        assert st == iso.ISO_ERR_WEIGHT
+
+
+def test_deterministic(torch):
+    y, _ = inputs.noisy(1, 300_000, 15)
+    _, a, ba = gpu_fit(torch, y)
+    _, b, bb = gpu_fit(torch, y)
+    assert np.array_equal(a, b) and np.array_equal(ba, bb)
+
+
+def test_iso_fit_blocking_entry(torch):
+    y, w = inputs.calibration(2, 9000, 16)
+    yt = torch.from_numpy(y).cuda()
+    wt = torch.from_numpy(w).cuda()
+    out = torch.empty_like(yt)
+    torch.cuda.synchronize()
+    st = iso.iso_fit(yt.data_ptr(), wt.data_ptr(), 2, 9000, out.data_ptr())
+    assert st == 0
+    _, z64, _ = oracle.fit_rows_f32(y, w)
+    assert fitcheck.parity(y, w, out.cpu().numpy(), z64)[0]
+    iso.iso_release()
+
+
+def test_fit_wrapper_on_torch_stream(torch):
+    y, _ = inputs.noisy(8, 7000, 17)
+    yt = torch.from_numpy(y).cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, bid = iso.fit(yt, block_ids=True, stream=s)
+    s.synchronize()
+    _, z64, _ = oracle.fit_rows_f32(y)
+    assert fitcheck.parity(y, None, out.cpu().numpy(), z64)[0]
