@@ -174,6 +174,16 @@ def main():
     iso.iso_timing_enable(True)
     run_steps(args.steps, True)
     phases = iso.iso_timing_read()
+    # the same, one row at a time, for a per-row breakdown
+    job_phases = {}
+    for j in jobs:
+        for _ in range(args.steps):
+            with torch.cuda.stream(stream):
+                flush.add_(1.0)
+            fit(j)
+        stream.synchronize()
+        jp = iso.iso_timing_read()
+        job_phases[j["label"]] = {k: round(v[0] / v[1], 5) for k, v in jp.items() if v[1] > 0}
     iso.iso_timing_enable(False)
     warm_total, _ = run_steps(args.steps, False)
 
@@ -184,6 +194,7 @@ def main():
         byt = e * (12 if j["w"] is not None else 8)
         rows_rep[j["label"]] = {
             "elements": e, "ms": round(t, 5), "elements_per_s": e / (t * 1e-3),
+            "kernel_ms": job_phases[j["label"]],
             "compulsory_gb_s": byt / (t * 1e-3) / 1e9,
             "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }

@@ -25,8 +25,8 @@ struct Plan {
     size_t off_row_flag = 0;
     // long rows
     size_t off_chunk_flag = 0, off_tot_S = 0, off_tot_W = 0, off_hull_cnt = 0;
-    size_t off_slot_idx = 0, off_slot_S = 0, off_slot_W = 0, off_st_S = 0, off_st_W = 0;
-    size_t off_desc = 0, off_node_cnt = 0, off_vb = 0, off_rec = 0;
+    size_t off_slot_idx = 0, off_slot_S = 0, off_slot_W = 0, off_st_S = 0, off_st_W = 0, off_win = 0;
+    size_t off_desc = 0, off_node_cnt = 0, off_vb = 0, off_rec = 0, off_desc_scr = 0, off_mi = 0;
     size_t off_cp_a = 0, off_cp_b = 0, off_cp_off = 0, off_cp_cnt = 0, off_cp_off2 = 0,
            off_cp_cnt2 = 0, off_cp_cut = 0, off_cp_cut2 = 0;
 };
@@ -63,12 +63,15 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
     p->off_slot_idx = take(SL * sizeof(uint16_t));
     p->off_slot_S = take(SL * sizeof(double));
     p->off_slot_W = weighted ? take(SL * sizeof(double)) : 0;
+    p->off_win = take(M * sizeof(iso::WinRec));
     p->off_st_S = take(M * sizeof(double));
     p->off_st_W = weighted ? take(M * sizeof(double)) : 0;
     p->off_desc = take(M * sizeof(uint2));
     p->off_node_cnt = take(M * sizeof(int32_t));
     p->off_vb = take(M * sizeof(int32_t));
     p->off_rec = take(M * sizeof(iso::ChunkRec));
+    p->off_desc_scr = take(M * sizeof(uint2));
+    p->off_mi = take(M * sizeof(int2));
     if (copy_control) {
         p->off_cp_a = take(SL * sizeof(uint4));
         p->off_cp_b = take(SL * sizeof(uint4));
@@ -97,12 +100,15 @@ iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control)
     ws.slot_idx = at<uint16_t>(base, p.off_slot_idx);
     ws.slot_S = at<double>(base, p.off_slot_S);
     ws.slot_W = weighted ? at<double>(base, p.off_slot_W) : nullptr;
+    ws.win = at<iso::WinRec>(base, p.off_win);
     ws.st_S = at<double>(base, p.off_st_S);
     ws.st_W = weighted ? at<double>(base, p.off_st_W) : nullptr;
     ws.desc = at<uint2>(base, p.off_desc);
     ws.node_cnt = at<int32_t>(base, p.off_node_cnt);
     ws.vb = at<int32_t>(base, p.off_vb);
     ws.rec = at<iso::ChunkRec>(base, p.off_rec);
+    ws.desc_scr = at<uint2>(base, p.off_desc_scr);
+    ws.merge_info = at<int2>(base, p.off_mi);
     ws.row_flag = at<int32_t>(base, p.off_row_flag);
     if (copy_control) {
         ws.cp_a = at<uint4>(base, p.off_cp_a);

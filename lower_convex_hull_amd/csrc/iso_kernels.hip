@@ -189,13 +189,33 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
     if (threadIdx.x == 0) sm.flag = 0;
 
     // ---- load (each thread its P consecutive elements) and check the data
+    float yr[P], wr[P];
+    const bool whole = base + P <= len;
+    if (P % 4 == 0 && whole && ((((uintptr_t)(gy + base)) | (WT ? (uintptr_t)(gw + base) : 0)) & 15u) == 0) {
+#pragma unroll
+        for (int q = 0; q < P / 4; ++q) {
+            float4 v = reinterpret_cast<const float4*>(gy + base)[q];
+            yr[4 * q] = v.x; yr[4 * q + 1] = v.y; yr[4 * q + 2] = v.z; yr[4 * q + 3] = v.w;
+            if (WT) {
+                float4 u = reinterpret_cast<const float4*>(gw + base)[q];
+                wr[4 * q] = u.x; wr[4 * q + 1] = u.y; wr[4 * q + 2] = u.z; wr[4 * q + 3] = u.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            int e = base + b;
+            yr[b] = e < len ? gy[e] : 0.0f;
+            if (WT) wr[b] = e < len ? gw[e] : 0.0f;
+        }
+    }
 #pragma unroll
     for (int b = 0; b < P; ++b) {
         int e = base + b;
         bool in = e < len;
-        float yy = in ? gy[e] : 0.0f;
+        float yy = yr[b];
         float ww = 1.0f;
-        if (WT) ww = in ? gw[e] : 0.0f;
+        if (WT) ww = wr[b];
         if (in) {
             if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
             if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
@@ -461,6 +481,13 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
     int total;
     int rank = wg_excl_scan_int<NT>(__popc(my), sm.ired, &total);
     const size_t slot = (size_t)gid * (C + 1);
+    const int h = total + 1;
+    WinRec* wr = ws.win + gid;
+    // window entry of hull rank r, or -1 if r is in the middle of a long hull
+    auto wslot = [&](int r) {
+        if (h <= 2 * kWinK || r < kWinK) return r;
+        return r >= h - kWinK ? kWinK + r - (h - kWinK) : -1;
+    };
     uint32_t bits = my;
     while (bits) {
         int b = lsb32(bits);
@@ -469,6 +496,8 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
         ws.slot_idx[slot + rank] = (uint16_t)min(k, len);
         ws.slot_S[slot + rank] = sm.S[k];
         if (WT) ws.slot_W[slot + rank] = sm.W[k];
+        const int e = wslot(rank);
+        if (e >= 0) wr->v[e] = make_double2(sm.S[k], WT ? sm.W[k] : (double)min(k, len));
         ++rank;
     }
     if (L == NT - 1) {
@@ -476,7 +505,9 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
         ws.slot_idx[slot + total] = (uint16_t)len;
         ws.slot_S[slot + total] = sm.S[C];
         if (WT) ws.slot_W[slot + total] = sm.W[C];
-        ws.hull_cnt[gid] = total + 1;
+        wr->v[wslot(total)] = make_double2(sm.S[C], WT ? sm.W[C] : (double)len);
+        wr->h = h;
+        ws.hull_cnt[gid] = h;
         ws.tot_S[gid] = sm.S[C];
         if (WT) ws.tot_W[gid] = sm.W[C];
         ws.chunk_flag[gid] = sm.flag;
@@ -502,21 +533,35 @@ struct Cur {
 };
 
 struct RowView {
-    const uint16_t* idx;
+    const uint16_t* idx;  // full slots (rarely read)
     const double* S;
     const double* W;
-    const double* stS;
+    const WinRec* win;    // compact hull ends
+    const int32_t* hc;    // hull vertex counts
+    const double* stS;    // chunk starts
     const double* stW;
     bool weighted;
 
-    // Vertex `pos` of chunk j's slot, in coordinates relative to chunk jr's
+    // Vertex `pos` of chunk j's hull, in coordinates relative to chunk jr's
     // start: the chunk-start difference first, then the chunk-relative part.
     __device__ __forceinline__ Pt vtx(int j, int pos, int jr) const {
-        size_t o = (size_t)j * (kChunk + 1) + pos;
+        const int h = hc[j];
+        int e = pos;
+        if (h > 2 * kWinK && pos >= kWinK) e = pos >= h - kWinK ? kWinK + pos - (h - kWinK) : -1;
+        double s, w;
+        if (e >= 0) {
+            const double2 v = win[j].v[e];
+            s = v.x;
+            w = v.y;
+        } else {
+            const size_t o = (size_t)j * (kChunk + 1) + pos;
+            s = S[o];
+            w = weighted ? W[o] : (double)idx[o];
+        }
         Pt p;
-        p.s = (stS[j] - stS[jr]) + S[o];
-        if (weighted) p.w = (stW[j] - stW[jr]) + W[o];
-        else p.w = (double)((int64_t)(j - jr) * kChunk + (int64_t)idx[o]);
+        p.s = (stS[j] - stS[jr]) + s;
+        if (weighted) p.w = (stW[j] - stW[jr]) + w;
+        else p.w = (double)((int64_t)(j - jr) * kChunk) + w;
         return p;
     }
 };
@@ -536,7 +581,7 @@ struct List {
     __device__ __forceinline__ Cur next(Cur c) const {
         return c.pos < dhi(d[c.seg]) ? Cur{c.seg, c.pos + 1} : Cur{c.seg + 1, dlo(d[c.seg + 1])};
     }
-    __device__ __forceinline__ Pt pt(const RowView& X, Cur c, int jr) const {
+    __device__ __forceinline__ Pt pt(const RowView X, Cur c, int jr) const {
         return X.vtx(dchunk(d[c.seg]), c.pos, jr);
     }
 };
@@ -545,7 +590,7 @@ struct List {
 // false then true along the range and true at Y: bisection over segments (by
 // each segment's last in-range vertex), then within one segment.
 template <class F>
-__device__ Cur find_first(const List& Lst, Cur X, Cur Y, F pred) {
+__device__ Cur find_first(const List Lst, Cur X, Cur Y, F pred) {
     int lo = X.seg, hi = Y.seg;
     while (lo < hi) {
         int mid = (lo + hi) >> 1;
@@ -563,87 +608,244 @@ __device__ Cur find_first(const List& Lst, Cur X, Cur Y, F pred) {
     return Cur{lo, plo};
 }
 
-// Merges the lists stored from slots a and b (b = a + span), writing the result
-// from slot a (Algorithm 1).
-__device__ void merge_lists(const RowView& X, uint2* desc, int32_t* cnt, int a, int b) {
-    List Lq{desc + a, cnt[a]};
-    List Rq{desc + b, cnt[b]};
-    const int jr = b;  // chunk of the shared point s
+// Bridge of the neighbouring lists L and R (Algorithm 1; Lemma 4.2): A is the
+// last vertex of L that stays, B the first vertex of R that stays.  In the
+// convex case A is the shared point s (kept once, in L) and B its successor.
+struct Bridge {
+    Cur A;
+    Cur B;
+};
+
+// Tests the chain at the shared point s.  Returns true when it is convex (the
+// bridge is then {A, B} as set); otherwise A, B are s's two neighbours, where
+// the walk starts.
+__device__ __forceinline__ bool bridge_start(const RowView X, const List Lq, const List Rq,
+                                             int jr, Cur& A, Cur& B) {
     Cur sL = Lq.last();
     Cur sR = Rq.first();
     Pt Ps = Rq.pt(X, sR, jr);
-    Cur A = Lq.prev(sL);  // every node has at least its two end points
-    Cur B = Rq.next(sR);
+    A = Lq.prev(sL);  // every node has at least its two end points
+    B = Rq.next(sR);
     Pt PA = Lq.pt(X, A, jr), PB = Rq.pt(X, B, jr);
     if (cross3(PA, Ps, PB) > 0.0) {
-        A = sL;  // convex at s: keep s once, in L
-    } else {
-        // walk (Lemma 4.2), at most kWalkCap steps
-        int steps = 0;
-        bool done = false;
-        for (;;) {
-            bool moved = false;
-            while (!Lq.is_first(A) && steps < kWalkCap) {
-                Cur A2 = Lq.prev(A);
-                Pt P2 = Lq.pt(X, A2, jr);
-                if (cross3(P2, PA, PB) <= 0.0) { A = A2; PA = P2; moved = true; ++steps; }
-                else break;
-            }
-            while (!Rq.is_last(B) && steps < kWalkCap) {
-                Cur B2 = Rq.next(B);
-                Pt P2 = Rq.pt(X, B2, jr);
-                if (cross3(PA, PB, P2) <= 0.0) { B = B2; PB = P2; moved = true; ++steps; }
-                else break;
-            }
-            if (!moved) { done = true; break; }
-            if (steps >= kWalkCap) break;
-        }
-        if (!done) {
-            // nested bisection (paper section 3.3, Theorem 5.2): a is the first
-            // vertex of L on whose tangent line to R its successor does not lie
-            // below; b is where that tangent touches R.
-            const Cur A0 = Lq.prev(sL);
-            const Cur B0 = Rq.next(sR);
-            const Cur RL = Rq.last();
-            auto tangent = [&](Pt Pa) -> Cur {
-                return find_first(Rq, B0, RL, [&](Cur r) -> bool {
-                    if (Rq.is_last(r)) return true;
-                    Pt Pr = Rq.pt(X, r, jr);
-                    Pt Pn = Rq.pt(X, Rq.next(r), jr);
-                    return cross3(Pa, Pr, Pn) > 0.0;
-                });
-            };
-            A = find_first(Lq, Lq.first(), A0, [&](Cur c) -> bool {
-                if (c.seg == A0.seg && c.pos == A0.pos) return true;
-                Pt Pc = Lq.pt(X, c, jr);
-                Cur t = tangent(Pc);
-                Pt Pt_ = Rq.pt(X, t, jr);
-                Pt Pn = Lq.pt(X, Lq.next(c), jr);
-                return cross3(Pc, Pt_, Pn) >= 0.0;
-            });
-            B = tangent(Lq.pt(X, A, jr));
-        }
+        A = sL;
+        return true;
     }
-    // cut L after A, R before B, move R's tail to follow L's list
-    uint2 dl = Lq.d[A.seg];
-    Lq.d[A.seg] = mkdesc(dchunk(dl), dlo(dl), A.pos);
-    uint2 dr = Rq.d[B.seg];
-    Rq.d[B.seg] = mkdesc(dchunk(dr), B.pos, dhi(dr));
-    const int nl = A.seg + 1;
-    const int nr = Rq.n - B.seg;
-    for (int i = 0; i < nr; ++i) Lq.d[nl + i] = Rq.d[B.seg + i];
-    cnt[a] = nl + nr;
+    return false;
 }
 
-template <bool WT>
+// The walk of Lemma 4.2 by one thread: A moves left while its turn towards B is
+// not strictly left, B moves right likewise, until neither moves.  Returns
+// false if it gives up after `cap` steps (A, B then hold where it stopped; a
+// resumed walk reaches the same bridge).
+__device__ __forceinline__ bool walk_thread(const RowView X, const List Lq, const List Rq, int jr, Cur& A,
+                            Cur& B, int cap) {
+    Pt PA = Lq.pt(X, A, jr), PB = Rq.pt(X, B, jr);
+    int steps = 0;
+    for (;;) {
+        bool moved = false;
+        while (!Lq.is_first(A) && steps < cap) {
+            Cur A2 = Lq.prev(A);
+            Pt P2 = Lq.pt(X, A2, jr);
+            if (cross3(P2, PA, PB) <= 0.0) { A = A2; PA = P2; moved = true; ++steps; }
+            else break;
+        }
+        while (!Rq.is_last(B) && steps < cap) {
+            Cur B2 = Rq.next(B);
+            Pt P2 = Rq.pt(X, B2, jr);
+            if (cross3(PA, PB, P2) <= 0.0) { B = B2; PB = P2; moved = true; ++steps; }
+            else break;
+        }
+        if (!moved) return true;
+        if (steps >= cap) return false;
+    }
+}
+
+// Nested bisection (paper section 3.3, Theorem 5.2): A is the first vertex of L
+// whose successor does not lie below A's tangent line to R; B is where that
+// tangent touches R.  Used when a walk gives up.
+__device__ __noinline__ Bridge bisect_bridge(const RowView X, const List Lq, const List Rq, int jr) {
+    const Cur sL = Lq.last();
+    const Cur sR = Rq.first();
+    const Cur A0 = Lq.prev(sL);
+    const Cur B0 = Rq.next(sR);
+    const Cur RL = Rq.last();
+    auto tangent = [&](Pt Pa) -> Cur {
+        return find_first(Rq, B0, RL, [&](Cur r) -> bool {
+            if (Rq.is_last(r)) return true;
+            Pt Pr = Rq.pt(X, r, jr);
+            Pt Pn = Rq.pt(X, Rq.next(r), jr);
+            return cross3(Pa, Pr, Pn) > 0.0;
+        });
+    };
+    Cur A = find_first(Lq, Lq.first(), A0, [&](Cur c) -> bool {
+        if (c.seg == A0.seg && c.pos == A0.pos) return true;
+        Pt Pc = Lq.pt(X, c, jr);
+        Cur t = tangent(Pc);
+        Pt Pt_ = Rq.pt(X, t, jr);
+        Pt Pn = Lq.pt(X, Lq.next(c), jr);
+        return cross3(Pc, Pt_, Pn) >= 0.0;
+    });
+    Cur B = tangent(Lq.pt(X, A, jr));
+    return Bridge{A, B};
+}
+
+// For the 64 lanes of a wave: the vertex `lane` positions before (dir < 0) or
+// after (dir > 0) cursor C along the list, or valid = false past its end.
+// Every lane of the wave must call it with the same C and dir.
+__device__ __forceinline__ Cur wave_offset(const List Lq, Cur C, int dir, int lane, bool& valid) {
+    const int sj = C.seg + dir * lane;
+    int cnt = 0;
+    if (sj >= 0 && sj < Lq.n) {
+        uint2 d = Lq.d[sj];
+        if (lane == 0) cnt = dir < 0 ? C.pos - dlo(d) + 1 : dhi(d) - C.pos + 1;
+        else cnt = dhi(d) - dlo(d) + 1;
+    }
+    int cum = cnt;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        int t = __shfl_up(cum, k);
+        if (lane >= k) cum += t;
+    }
+    const int total = __shfl(cum, 63);
+    valid = lane < total;
+    // j = number of segments whose cumulative count is <= lane
+    int j = 0;
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) {
+        int c = __shfl(cum, j + k - 1);
+        if (c <= lane) j += k;
+    }
+    int before = __shfl(cum, j > 0 ? j - 1 : 0);
+    if (j == 0) before = 0;
+    if (!valid) return C;
+    const int seg = C.seg + dir * j;
+    const uint2 d = Lq.d[seg];
+    const int top = (j == 0) ? C.pos : (dir < 0 ? dhi(d) : dlo(d));
+    return Cur{seg, top + dir * (lane - before)};
+}
+
+__device__ __forceinline__ Pt shfl_down_pt(Pt p, int k) {
+    return Pt{__shfl_down(p.w, k), __shfl_down(p.s, k)};
+}
+__device__ __forceinline__ Cur bcast_cur(Cur c, int src) {
+    return Cur{__shfl(c.seg, src), __shfl(c.pos, src)};
+}
+
+// The same walk by a whole wave: each step tests the next 63 candidates at
+// once (the pages' warp-per-merge search, section 3.3, on 64 lanes).  The
+// candidate where a sequential walk would stop is the first lane whose test
+// holds.  Returns false if it gives up after `cap` steps.
+__device__ __forceinline__ bool walk_wave(const RowView X, const List Lq, const List Rq, int jr, Cur& A, Cur& B,
+                          int cap) {
+    const int lane = threadIdx.x & 63;
+    int steps = 0;
+    for (;;) {
+        bool moved = false;
+        // A moves left
+        for (;;) {
+            Pt PB = Rq.pt(X, B, jr);
+            bool valid;
+            Cur v = wave_offset(Lq, A, -1, lane, valid);
+            Pt Pv = valid ? Lq.pt(X, v, jr) : Pt{0.0, 0.0};
+            Pt Pu = shfl_down_pt(Pv, 1);
+            bool vnext = __shfl_down((int)valid, 1) != 0;
+            bool stop = valid && lane < 63 && (!vnext || cross3(Pu, Pv, PB) > 0.0);
+            unsigned long long bal = __ballot(stop);
+            if (bal) {
+                int i = __ffsll((long long)bal) - 1;
+                if (i > 0) moved = true;
+                A = bcast_cur(v, i);
+                break;
+            }
+            A = bcast_cur(v, 63);
+            moved = true;
+            if (++steps >= cap) return false;
+        }
+        // B moves right
+        for (;;) {
+            Pt PA = Lq.pt(X, A, jr);
+            bool valid;
+            Cur v = wave_offset(Rq, B, +1, lane, valid);
+            Pt Pv = valid ? Rq.pt(X, v, jr) : Pt{0.0, 0.0};
+            Pt Pn = shfl_down_pt(Pv, 1);
+            bool vnext = __shfl_down((int)valid, 1) != 0;
+            bool stop = valid && lane < 63 && (!vnext || cross3(PA, Pv, Pn) > 0.0);
+            unsigned long long bal = __ballot(stop);
+            if (bal) {
+                int i = __ffsll((long long)bal) - 1;
+                if (i > 0) moved = true;
+                B = bcast_cur(v, i);
+                break;
+            }
+            B = bcast_cur(v, 63);
+            moved = true;
+            if (++steps >= cap) return false;
+        }
+        if (!moved) return true;
+    }
+}
+
+// Writes the cut of one merge: L ends at A, R starts at B; records what the
+// descriptor move needs.
+__device__ __forceinline__ void apply_cut(uint2* D, int32_t* CNT, int2* MI, int k, int a, int b,
+                                          int nR, Bridge br) {
+    uint2 dl = D[a + br.A.seg];
+    D[a + br.A.seg] = mkdesc(dchunk(dl), dlo(dl), br.A.pos);
+    uint2 dr = D[b + br.B.seg];
+    D[b + br.B.seg] = mkdesc(dchunk(dr), br.B.pos, dhi(dr));
+    MI[k] = make_int2(br.A.seg + 1, br.B.seg);
+    CNT[a] = br.A.seg + 1 + (nR - br.B.seg);
+}
+
+// Keeps a loaded value alive so the load that warms the cache is not removed.
+__device__ __forceinline__ void keep(double v) { asm volatile("" ::"v"(v)); }
+
+// One workgroup per row runs every level of the merge tree.  Segment lists
+// live in LDS when the row has at most kMergeLdsMax chunks (else in the
+// workspace).  Per level: one thread per merge finds its bridge and cuts the two
+// boundary segments in place; then teams of threads move each right list's
+// remaining descriptors down behind the left list's (through a scratch copy,
+// since the two ranges may overlap).
+template <bool WT, bool INLDS>
 __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     constexpr int NT = kMergeNT;
+    extern __shared__ uint2 dyn_lds[];
     __shared__ double red[NT / 64 + 1];
     __shared__ int ired[NT / 64 + 1];
     __shared__ int sflag;
+    __shared__ int s_nhard;
+    __shared__ int4 s_hard[kHardCap];
+    constexpr int NW = NT / 64;
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m;
     const int tid = threadIdx.x;
+    const int wid = tid >> 6, wlane = tid & 63;
+
+    uint2* D;
+    uint2* SCR;
+    int32_t* CNT;
+    int2* MI;
+    int32_t* HC;
+    double* STS;
+    double* STW;
+    if (INLDS) {
+        D = dyn_lds;
+        SCR = D + m;
+        MI = reinterpret_cast<int2*>(SCR + m);
+        STS = reinterpret_cast<double*>(MI + (m / 2 + 1));
+        STW = STS + m;  // used when weighted
+        CNT = reinterpret_cast<int32_t*>(STW + (WT ? m : 0));
+        HC = CNT + m;
+    } else {
+        D = ws.desc + rb;
+        SCR = ws.desc_scr + rb;
+        CNT = ws.node_cnt + rb;
+        MI = ws.merge_info + rb;
+        HC = ws.hull_cnt + rb;
+        STS = ws.st_S + rb;
+        STW = WT ? ws.st_W + rb : nullptr;
+    }
 
     // ---- row flags, chunk starts (exclusive scan of the chunk totals)
     if (tid == 0) sflag = 0;
@@ -657,44 +859,116 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
         double vs = j < m ? ws.tot_S[rb + j] : 0.0;
         double tot;
         double xs = wg_excl_scan<NT>(vs, red, &tot);
-        if (j < m) ws.st_S[rb + j] = carryS + xs;
+        if (j < m) STS[j] = carryS + xs;
         carryS += tot;
         if (WT) {
             double vw = j < m ? ws.tot_W[rb + j] : 0.0;
             double xw = wg_excl_scan<NT>(vw, red, &tot);
-            if (j < m) ws.st_W[rb + j] = carryW + xw;
+            if (j < m) STW[j] = carryW + xw;
             carryW += tot;
         }
     }
     for (int j = tid; j < m; j += NT) {
-        ws.desc[rb + j] = mkdesc(j, 0, ws.hull_cnt[rb + j] - 1);
-        ws.node_cnt[rb + j] = 1;
+        const int h = ws.hull_cnt[rb + j];
+        if (INLDS) HC[j] = h;
+        D[j] = mkdesc(j, 0, h - 1);
+        CNT[j] = 1;
+    }
+    // warm this XCD's L2 with the compact hull ends of the whole row
+    {
+        const double2* wv = reinterpret_cast<const double2*>(ws.win + rb);
+        const int nv2 = m * (int)(sizeof(WinRec) / sizeof(double2));
+        double acc = 0.0;
+        for (int i = tid; i < nv2; i += NT) acc += wv[i].x;
+        keep(acc);
     }
     __syncthreads();
     if (tid == 0) ws.row_flag[row] = sflag;
 
-    RowView X{ws.slot_idx + rb * (kChunk + 1), ws.slot_S + rb * (kChunk + 1),
-              WT ? ws.slot_W + rb * (kChunk + 1) : nullptr, ws.st_S + rb,
-              WT ? ws.st_W + rb : nullptr, WT};
-    uint2* desc = ws.desc + rb;
-    int32_t* cnt = ws.node_cnt + rb;
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
+              STS, WT ? STW : nullptr, WT};
 
     // ---- the merge tree, level by level
     for (int span = 1; span < m; span <<= 1) {
         const int nm = (m - span + 2 * span - 1) / (2 * span);
-        for (int k = tid; k < nm; k += NT) merge_lists(X, desc, cnt, 2 * k * span, 2 * k * span + span);
+        if (nm > NW) {
+            // many merges: a thread each; walks that run long go to the waves
+            if (tid == 0) s_nhard = 0;
+            __syncthreads();
+            for (int k = tid; k < nm; k += NT) {
+                const int a = 2 * k * span, b = a + span;
+                List Lq{D + a, CNT[a]};
+                List Rq{D + b, CNT[b]};
+                Bridge br;
+                if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
+                    !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
+                    int h = atomicAdd(&s_nhard, 1);
+                    if (h < kHardCap) {
+                        s_hard[h] = make_int4(k, br.A.seg, br.A.pos, (br.B.seg << 16) | br.B.pos);
+                        continue;
+                    }
+                    br = bisect_bridge(X, Lq, Rq, b);
+                }
+                apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+            __syncthreads();
+            const int nh = min(s_nhard, kHardCap);
+            for (int h = wid; h < nh; h += NW) {
+                const int4 hk = s_hard[h];
+                const int k = hk.x, a = 2 * k * span, b = a + span;
+                List Lq{D + a, CNT[a]};
+                List Rq{D + b, CNT[b]};
+                Bridge br{Cur{hk.y, hk.z}, Cur{hk.w >> 16, hk.w & 0xffff}};
+                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                    br = bisect_bridge(X, Lq, Rq, b);
+                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+        } else {
+            // few merges: a wave each
+            for (int k = wid; k < nm; k += NW) {
+                const int a = 2 * k * span, b = a + span;
+                List Lq{D + a, CNT[a]};
+                List Rq{D + b, CNT[b]};
+                Bridge br;
+                if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
+                    if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                        br = bisect_bridge(X, Lq, Rq, b);
+                }
+                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+        }
+        __syncthreads();
+        // move the right lists' tails: teams of ts threads per merge
+        int ts = NT / nm;
+        ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
+        const int teams = NT / ts;
+        const int lane = tid & (ts - 1);
+        for (int k = tid / ts; k < nm; k += teams) {
+            const int b = (2 * k + 1) * span;
+            const int rs = MI[k].y;
+            const int nr = CNT[b] - rs;
+            for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
+        }
+        __syncthreads();
+        for (int k = tid / ts; k < nm; k += teams) {
+            const int a = 2 * k * span, b = a + span;
+            const int nl = MI[k].x;
+            const int nr = CNT[b] - MI[k].y;
+            for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
+        }
         __syncthreads();
     }
 
     // ---- reconstruction records (Corollary 4.5)
-    const int nroot = cnt[0];
+    const int nroot = CNT[0];
     int carry = 0;
     int32_t* vb = ws.vb + rb;
     for (int t0 = 0; t0 < nroot; t0 += NT) {
         int i = t0 + tid;
         int v = 0;
         if (i < nroot) {
-            uint2 d = desc[i];
+            uint2 d = D[i];
             v = dhi(d) - dlo(d) + 1;
         }
         int tot;
@@ -708,11 +982,11 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
         int lo = 0, hi = nroot - 1;
         while (lo < hi) {
             int mid = (lo + hi) >> 1;
-            if (dchunk(desc[mid]) >= j) hi = mid;
+            if (dchunk(D[mid]) >= j) hi = mid;
             else lo = mid + 1;
         }
         const int i = lo;
-        const uint2 d = desc[i];
+        const uint2 d = D[i];
         ChunkRec rc;
         rc.pad = 0;
         rc.vb = vb[i];
@@ -722,12 +996,12 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
             rc.slope_in = 0.0;
             rc.slope_out = 0.0;
             if (i > 0) {
-                uint2 p = desc[i - 1];
+                uint2 p = D[i - 1];
                 Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
                 rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
             }
             if (i + 1 < nroot) {
-                uint2 q = desc[i + 1];
+                uint2 q = D[i + 1];
                 Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
                 rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
             }
@@ -735,7 +1009,7 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
             // the chunk lies under one edge, from the last vertex of the
             // previous segment to the first vertex of the next (i >= 1: chunk 0
             // always holds the row's first point)
-            uint2 p = desc[i - 1];
+            uint2 p = D[i - 1];
             Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
             rc.lo = -1;
             rc.hi = -1;
@@ -754,7 +1028,8 @@ template <bool WT>
 __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
                                                     float* __restrict__ out,
                                                     int32_t* __restrict__ block_id) {
-    constexpr int NT = kLongNT, P = kLongP, C = kChunk;
+    constexpr int NT = kLongNT, C = kChunk;
+    constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
     __shared__ int vidx[C + 1];
     __shared__ float vslope[C + 1];
     const int64_t gid = blockIdx.x;
@@ -765,26 +1040,37 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
     float* go = out + off;
     int32_t* gb = block_id ? block_id + off : nullptr;
     const int tid = threadIdx.x;
-    const int e0 = tid * P;
-    if (ws.row_flag[row] & kFlagNonfinite) {
-        for (int b = 0; b < P; ++b) {
-            int e = e0 + b;
-            if (e < len) {
-                go[e] = __builtin_nanf("");
-                if (gb) gb[e] = -1;
+    // element groups e = 4 * (g * NT + tid): consecutive threads write
+    // consecutive 16-byte groups
+    const bool vec = ((((uintptr_t)go) | (uintptr_t)gb) & 15u) == 0;
+    auto store4 = [&](int e, float4 v, int4 b) {
+        if (vec && e + 4 <= len) {
+            *reinterpret_cast<float4*>(go + e) = v;
+            if (gb) *reinterpret_cast<int4*>(gb + e) = b;
+        } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+            const int bb[4] = {b.x, b.y, b.z, b.w};
+            for (int t = 0; t < 4 && e + t < len; ++t) {
+                go[e + t] = vv[t];
+                if (gb) gb[e + t] = bb[t];
             }
+        }
+    };
+    if (ws.row_flag[row] & kFlagNonfinite) {
+        const float nan = __builtin_nanf("");
+        for (int g = 0; g < G; ++g) {
+            int e = 4 * (g * NT + tid);
+            if (e < len) store4(e, make_float4(nan, nan, nan, nan), make_int4(-1, -1, -1, -1));
         }
         return;
     }
     const ChunkRec rc = ws.rec[gid];
     if (rc.lo < 0) {
         const float v = sign * (float)rc.slope_in;
-        for (int b = 0; b < P; ++b) {
-            int e = e0 + b;
-            if (e < len) {
-                go[e] = v;
-                if (gb) gb[e] = rc.vb - 1;
-            }
+        const int b = rc.vb - 1;
+        for (int g = 0; g < G; ++g) {
+            int e = 4 * (g * NT + tid);
+            if (e < len) store4(e, make_float4(v, v, v, v), make_int4(b, b, b, b));
         }
         return;
     }
@@ -795,27 +1081,39 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         double ds = ws.slot_S[slot + v + 1] - ws.slot_S[slot + v];
         double dw = WT ? ws.slot_W[slot + v + 1] - ws.slot_W[slot + v]
                        : (double)((int)ws.slot_idx[slot + v + 1] - (int)ws.slot_idx[slot + v]);
-        vslope[v] = (float)(ds / dw);
+        vslope[v] = sign * (float)(ds / dw);
     }
     __syncthreads();
-    if (e0 >= len) return;
-    // q = number of the chunk's surviving vertices at or before e0
-    int lo = 0, hi = nv;
-    while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (vidx[mid] <= e0) lo = mid + 1;
-        else hi = mid;
+    const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
+    for (int g = 0; g < G; ++g) {
+        const int e0 = 4 * (g * NT + tid);
+        if (e0 >= len) break;
+        // q = number of the chunk's surviving vertices at or before e0
+        int lo = 0, hi = nv;
+        while (lo < hi) {
+            int mid = (lo + hi) >> 1;
+            if (vidx[mid] <= e0) lo = mid + 1;
+            else hi = mid;
+        }
+        int q = lo;
+        float vv[4];
+        int bb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int e = e0 + t;
+            while (q < nv && vidx[q] <= e) ++q;
+            vv[t] = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
+            bb[t] = rc.vb + q - 1;
+        }
+        store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
     }
-    int q = lo;
-    const float sin_ = (float)rc.slope_in, sout = (float)rc.slope_out;
-    for (int b = 0; b < P; ++b) {
-        int e = e0 + b;
-        if (e >= len) break;
-        while (q < nv && vidx[q] <= e) ++q;
-        float v = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
-        go[e] = sign * v;
-        if (gb) gb[e] = rc.vb + q - 1;
-    }
+}
+
+size_t merge_lds_bytes(int m, bool weighted) {
+    // D, SCR (8 B each), MI (8 B per merge), STS (8 B), STW (8 B, weighted),
+    // CNT, HC (4 B each)
+    return (size_t)m * 16 + (size_t)(m / 2 + 1) * 8 + (size_t)m * (weighted ? 16 : 8) +
+           (size_t)m * 8;
 }
 
 template <int NT, int P>
@@ -858,12 +1156,31 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
                            sh.sign, ws);
     timed_end(st);
     timed_begin(2, st);
-    if (wt)
-        hipLaunchKernelGGL(k_merge_rows<true>, dim3((unsigned)sh.rows), dim3(kMergeNT), 0, st, sh.m,
-                           ws);
-    else
-        hipLaunchKernelGGL(k_merge_rows<false>, dim3((unsigned)sh.rows), dim3(kMergeNT), 0, st,
-                           sh.m, ws);
+    if (sh.m <= kMergeLdsMax) {
+        const size_t lds = merge_lds_bytes(sh.m, wt);
+        static bool attr_set = false;
+        if (!attr_set) {
+            const int maxb = (int)merge_lds_bytes(kMergeLdsMax, true);
+            (void)hipFuncSetAttribute((const void*)k_merge_rows<true, true>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
+            (void)hipFuncSetAttribute((const void*)k_merge_rows<false, true>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
+            attr_set = true;
+        }
+        if (wt)
+            hipLaunchKernelGGL((k_merge_rows<true, true>), dim3((unsigned)sh.rows), dim3(kMergeNT), lds,
+                               st, sh.m, ws);
+        else
+            hipLaunchKernelGGL((k_merge_rows<false, true>), dim3((unsigned)sh.rows), dim3(kMergeNT),
+                               lds, st, sh.m, ws);
+    } else {
+        if (wt)
+            hipLaunchKernelGGL((k_merge_rows<true, false>), dim3((unsigned)sh.rows), dim3(kMergeNT), 0,
+                               st, sh.m, ws);
+        else
+            hipLaunchKernelGGL((k_merge_rows<false, false>), dim3((unsigned)sh.rows), dim3(kMergeNT),
+                               0, st, sh.m, ws);
+    }
     timed_end(st);
     timed_begin(3, st);
     if (wt)

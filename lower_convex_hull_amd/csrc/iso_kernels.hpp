@@ -15,8 +15,12 @@ constexpr int kLongNT = 256;
 constexpr int kLongP = 16;
 constexpr int kChunk = kLongNT * kLongP;  // 4096
 constexpr int kShortMax = 4096;
-constexpr int kMergeNT = 256;
-constexpr int kWalkCap = 64;  // walk steps before the merge switches to bisection
+constexpr int kMergeNT = 1024;
+constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
+constexpr int kWinK = 8;            // hull vertices kept at each end of a chunk's window
+constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed to a wave
+constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
+constexpr int kHardCap = 256;     // merges per level a wave may take over
 
 // Per-row data flags written by the kernels (read back by the checking path).
 constexpr int kFlagNonfinite = 1;
@@ -38,6 +42,16 @@ struct ChunkRec {
     double slope_out;
 };
 
+// A chunk hull's two ends in one compact record: its vertex count h and the
+// chunk-relative (S, W) of its first kWinK and last kWinK vertices (all of them
+// when h <= 2 kWinK).  The merge tree reads vertices here; only walks that
+// reach the middle of a long chunk hull read the full slot.
+struct WinRec {
+    int32_t h;
+    int32_t pad[3];
+    double2 v[2 * kWinK];
+};
+
 // Device pointers of the long-row workspace (see plan_long in iso_api.hip).
 struct LongWs {
     int32_t* chunk_flag;  // [R*m]
@@ -47,11 +61,14 @@ struct LongWs {
     uint16_t* slot_idx;   // [R*m*(C+1)] chunk-relative point index of each vertex
     double* slot_S;       // [R*m*(C+1)] chunk-relative S of each vertex
     double* slot_W;       // [R*m*(C+1)] chunk-relative W (weighted only)
+    WinRec* win;          // [R*m] ends of each chunk hull
     double* st_S;         // [R*m] chunk starts (exclusive scan of totals)
     double* st_W;         // [R*m] (weighted only)
     uint2* desc;          // [R*m] segment descriptors (chunk, lo | hi << 16)
     int32_t* node_cnt;    // [R*m] segments in the list stored from this slot
     int32_t* vb;          // [R*m] scratch: vertex prefix over the root list
+    uint2* desc_scr;      // [R*m] scratch for descriptor moves (lists in the workspace)
+    int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
     // grid-copy control only

@@ -169,6 +169,28 @@ def test_batch_of_long_rows(torch):
     check(torch, y2, None, name="long-batch-noisy")
 
 
+def test_long_walks_and_bisection(torch):
+    """Dense (strictly increasing) rows with cliffs: a merge then removes thousands
+    of vertices, so walks exceed their caps and the wave walk and the nested
+    bisection run (at low and at high levels of the merge tree)."""
+    rng = np.random.default_rng(21)
+    for n, cliffs in ((300_000, (8191, 40_000, 123_457, 299_999)), (70_000, (4095, 69_999)),
+                      (1_000_000, (524_287, 999_999))):
+        y, _ = inputs.dense(n, 22)
+        y = y.copy()
+        for c in cliffs:
+            y[0, c] = -float(rng.uniform(50, 500))
+        check(torch, y, None, name=f"cliffs/{n}")
+        w = inputs.weights("exp", n, 23)[None, :]
+        check(torch, y, w, name=f"cliffs-w/{n}")
+
+
+def test_sawtooth_and_walk_families_at_1e6(torch):
+    for fam in ("sawtooth", "random_walk", "cliff", "piecewise"):
+        y = inputs.family(fam, 1_000_000, 24)[None, :]
+        check(torch, y, None, name=f"{fam}/1e6", block_ids=False)
+
+
 def test_decreasing_flag(torch):
     y, _ = inputs.noisy(4, 3000, 9)
     check(torch, y[:, ::-1].copy(), None, flags=iso.ISO_F_DECREASING, name="dec-short")
