@@ -73,8 +73,9 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
     p->off_desc_scr = take(M * sizeof(uint2));
     p->off_mi = take(M * sizeof(int2));
     if (copy_control) {
-        p->off_cp_a = take(SL * sizeof(uint4));
-        p->off_cp_b = take(SL * sizeof(uint4));
+        const size_t vb = weighted ? 24 : 16;  // bytes of one flat-array vertex
+        p->off_cp_a = take(SL * vb);
+        p->off_cp_b = take(SL * vb);
         p->off_cp_off = take(M * sizeof(int32_t));
         p->off_cp_cnt = take(M * sizeof(int32_t));
         p->off_cp_off2 = take(M * sizeof(int32_t));
@@ -111,8 +112,8 @@ iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control)
     ws.merge_info = at<int2>(base, p.off_mi);
     ws.row_flag = at<int32_t>(base, p.off_row_flag);
     if (copy_control) {
-        ws.cp_a = at<uint4>(base, p.off_cp_a);
-        ws.cp_b = at<uint4>(base, p.off_cp_b);
+        ws.cp_a = at<char>(base, p.off_cp_a);
+        ws.cp_b = at<char>(base, p.off_cp_b);
         ws.cp_off = at<int32_t>(base, p.off_cp_off);
         ws.cp_cnt = at<int32_t>(base, p.off_cp_cnt);
         ws.cp_off2 = at<int32_t>(base, p.off_cp_off2);

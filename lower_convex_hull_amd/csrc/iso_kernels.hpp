@@ -72,8 +72,8 @@ struct LongWs {
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
     // grid-copy control only
-    uint4* cp_a;          // [R*m*(C+1)] flat vertex buffers (ping)
-    uint4* cp_b;          // (pong)
+    void* cp_a;           // [R*m*(C+1)] flat vertex buffers (ping), 16 B (24 B weighted) each
+    void* cp_b;           // (pong)
     int32_t* cp_off;      // [R*m] node offsets (ping)
     int32_t* cp_cnt;      // [R*m] node vertex counts (ping)
     int32_t* cp_off2;     // [R*m] (pong)
@@ -90,6 +90,10 @@ struct LongShape {
     float sign;    // +1 increasing, -1 decreasing
 };
 
+// Phases of the launch timing (the ISO_PHASE_* values of iso.h).
+constexpr int kPhaseShort = 0, kPhaseChunk = 1, kPhaseMerge = 2, kPhaseExpand = 3,
+              kPhaseCopyBridge = 4, kPhaseCopyMove = 5;
+
 // Launch timing for benchmarks (iso_timing_enable / iso_timing_read): when
 // enabled, timed_begin records an event before a launch and timed_end one
 // after it, on the launch's stream.
@@ -98,6 +102,10 @@ void timed_end(hipStream_t st);
 
 hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                         float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
+
+// The merge phase of the vertex-copying control (iso_copy.hip); leaves the
+// reconstruction records in ws.rec like the segment-list merge.
+hipError_t launch_copy_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
 
 hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
                        float* out, int32_t* block_id, bool copy_control, hipStream_t st);

@@ -191,6 +191,34 @@ def test_sawtooth_and_walk_families_at_1e6(torch):
         check(torch, y, None, name=f"{fam}/1e6", block_ids=False)
 
 
+@pytest.mark.parametrize("case", ["c3", "c4", "c5x8", "families", "cliffs"])
+def test_copy_control_matches(torch, case):
+    """The vertex-copying merge control (ISO_F_COPY_CONTROL) gives the oracle's fit,
+    and the same output as the segment-list merge."""
+    if case == "c3":
+        ys = [inputs.config("c3_row1e7_noisy")]
+    elif case == "c4":
+        ys = [inputs.config("c4_row1e7_dense")]
+    elif case == "c5x8":
+        ys = [inputs.config("c5_calib256x2p20", rows=8)]
+    elif case == "families":
+        ys = [(inputs.family(f, 123_457, 5)[None, :], inputs.weights(wk, 123_457, 5))
+              for f in ("gaussian", "random_walk", "sawtooth", "cliff") for wk in ("none", "exp")]
+    else:
+        y, _ = inputs.dense(300_000, 22)
+        y = y.copy()
+        for c in (8191, 40_000, 299_999):
+            y[0, c] = -100.0
+        ys = [(y, None)]
+    for y, w in ys:
+        if w is not None:
+            w = np.asarray(w).reshape(y.shape)
+        out_c, bid_c, _ = check(torch, y, w, flags=iso.ISO_F_COPY_CONTROL, name=f"copy/{case}")
+        st, out_s, bid_s = gpu_fit(torch, y, w)
+        assert st == 0
+        assert np.array_equal(out_c, out_s), f"copy/{case}: outputs differ from the segment-list merge"
+
+
 def test_decreasing_flag(torch):
     y, _ = inputs.noisy(4, 3000, 9)
     check(torch, y[:, ::-1].copy(), None, flags=iso.ISO_F_DECREASING, name="dec-short")
