@@ -146,11 +146,12 @@ int64_t iso_short_row_max(void);
 enum {
     ISO_PHASE_SHORT_ROWS = 0,  /* whole short rows in one kernel          */
     ISO_PHASE_CHUNK_HULLS = 1, /* prefix sums, chunk hulls, chunk slots   */
-    ISO_PHASE_MERGE = 2,       /* segment-list merge tree + chunk records */
+    ISO_PHASE_MERGE = 2,       /* segment-list merge (first stage) or its control's set-up */
     ISO_PHASE_EXPAND = 3,      /* slope expansion (the fit)               */
     ISO_PHASE_COPY_BRIDGE = 4, /* copy control: bridges of one level      */
     ISO_PHASE_COPY_MOVE = 5,   /* copy control: vertex rewrite of a level */
-    ISO_PHASE_COUNT = 6
+    ISO_PHASE_MERGE_TOP = 6,   /* second merge stage (group hulls of a row) */
+    ISO_PHASE_COUNT = 7
 };
 int iso_timing_enable(int on);
 int iso_timing_read(double* ms, int64_t* launches, int nphase);

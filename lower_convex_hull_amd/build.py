@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libiso.so")
-SOURCES = ["iso_api.hip", "iso_kernels.hip", "iso_copy.hip"]
+SOURCES = ["iso_api.hip", "iso_kernels.hip", "iso_merge.hip", "iso_copy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

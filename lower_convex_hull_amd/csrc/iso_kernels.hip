@@ -38,16 +38,25 @@ namespace {
 // ----------------------------------------------------------------------------
 template <int NT, int P, bool WT>
 struct HullSmem {
-    double S[NT * P + 1];            // block-relative S_k
-    double W[WT ? NT * P + 1 : 1];   // block-relative W_k (weighted only)
+    // block-relative S_k and W_k, stored at sk(k) = k + k / P: each thread's
+    // points plus one pad slot, so that threads reading their own points (and
+    // walkers reading points P apart) hit different LDS banks
+    double S[NT * (P + 1) + 1];
+    double W[WT ? NT * (P + 1) + 1 : 1];
+    int16_t prv[NT * P + 1];        // hull neighbours of each vertex (the walks' links)
+    int16_t nxt[NT * P + 1];
     uint32_t mask[NT];
-    uint32_t occ[(NT + 31) / 32];    // bit L: mask[L] != 0
-    int32_t blo[NT];                 // bridge ends of the merge led by thread L
-    int32_t bhi[NT];
+    int16_t bra[2 * NT];            // bridge ends of every merge, by round
+    int16_t brb[2 * NT];
     double red[NT / 64 + 1];
     int ired[NT / 64 + 1];
     int flag;
 };
+
+template <int P>
+__device__ __forceinline__ int sk(int k) {
+    return k + k / P;
+}
 
 template <int NT, int P, bool WT>
 struct Block {
@@ -56,56 +65,18 @@ struct Block {
 
     __device__ __forceinline__ Pt pt(int k) const {
         Pt p;
-        p.s = sm.S[k];
-        p.w = WT ? sm.W[k] : (double)min(k, len);
+        p.s = sm.S[sk<P>(k)];
+        p.w = WT ? sm.W[sk<P>(k)] : (double)min(k, len);
         return p;
     }
-
-    // Highest vertex below point k, searching threads >= lo_lane.
-    __device__ int prev_vertex(int k, int lo_lane) const {
-        int Lk = k / P;
-        int b = k - Lk * P;
-        if (Lk < NT && b > 0) {
-            uint32_t m = sm.mask[Lk] & ((1u << b) - 1u);
-            if (m) return Lk * P + msb32(m);
-        }
-        int x = Lk - 1;
-        while (x >= lo_lane) {
-            int wi = x >> 5;
-            uint32_t word = sm.occ[wi] & ((2u << (x & 31)) - 1u);
-            if (word) {
-                int c = (wi << 5) + msb32(word);
-                if (c < lo_lane) break;
-                return c * P + msb32(sm.mask[c]);
-            }
-            x = (wi << 5) - 1;
-        }
-        return lo_lane * P;  // the group's first point is always a vertex
-    }
-
-    // Lowest vertex above point k among threads < hi_lane, else the group's
-    // last point hi_lane*P.
-    __device__ int next_vertex(int k, int hi_lane) const {
-        int Lk = k / P;
-        int b = k - Lk * P;
-        if (Lk < hi_lane) {
-            uint32_t m = sm.mask[Lk] & ~((2u << b) - 1u);
-            if (m) return Lk * P + lsb32(m);
-        }
-        int x = Lk + 1;
-        while (x < hi_lane) {
-            int wi = x >> 5;
-            uint32_t word = sm.occ[wi] & ~((1u << (x & 31)) - 1u);
-            if (word) {
-                int c = (wi << 5) + lsb32(word);
-                if (c >= hi_lane) break;
-                return c * P + lsb32(sm.mask[c]);
-            }
-            x = (wi + 1) << 5;
-        }
-        return hi_lane * P;
-    }
 };
+
+// Makes one lane's LDS writes visible to the other lanes of its wave and keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
 
 // Loads the block's elements, forms the block-relative cumulative sums, and
 // leaves in sm.mask the vertices of the block's lower hull.  Returns this
@@ -178,8 +149,8 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
     if (WT) xw = wg_excl_scan<NT>(lw, sm.red, &tot);
 #pragma unroll
     for (int b = 0; b < P; ++b) {
-        sm.S[base + b + 1] = xs + ps[b];
-        if (WT) sm.W[base + b + 1] = xw + pw[b];
+        sm.S[sk<P>(base + b + 1)] = xs + ps[b];
+        if (WT) sm.W[sk<P>(base + b + 1)] = xw + pw[b];
     }
     if (L == 0) {
         sm.S[0] = 0.0;
@@ -248,67 +219,86 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
     }
     uint32_t my = stk & ((1u << P) - 1u);
     sm.mask[L] = my;
+    __syncthreads();
+
+    // ---- links between consecutive vertices of the thread hulls; a thread's
+    // last point is the next thread's first (bit 0, always a vertex)
     {
-        unsigned long long bal = __ballot(my != 0u);
-        if ((L & 31) == 0) sm.occ[L >> 5] = (uint32_t)(bal >> (L & 32));
+        const uint32_t pm = L > 0 ? sm.mask[L - 1] : 0u;
+        int prev_v = L > 0 ? (L - 1) * P + msb32(pm) : 0;
+        uint32_t bits = my;
+        while (bits) {
+            const int b = lsb32(bits);
+            bits &= bits - 1u;
+            const int k = base + b;
+            sm.prv[k] = (int16_t)prev_v;
+            sm.nxt[k] = (int16_t)(bits ? base + lsb32(bits) : base + P);
+            prev_v = k;
+        }
+        if (L == NT - 1) sm.prv[NT * P] = (int16_t)prev_v;
     }
     __syncthreads();
 
     // ---- merge the thread hulls pairwise (paper section 3.2; Lemma 4.2's
-    // walk).  The first thread of each pair of groups walks to the bridge;
-    // then every thread clears its bits strictly inside the bridge.
-    for (int r = 0; (1 << r) < NT; ++r) {
+    // walk).  The first thread of each pair of groups walks to the bridge over
+    // the links and relinks its two ends; the rounds inside a wave need no
+    // workgroup barrier.  The removed vertices' bits are cleared at the end.
+    constexpr int R = __builtin_ctz(NT);
+    for (int r = 0; r < R; ++r) {
         const int g = 2 << r, half = 1 << r;
         if ((L & (g - 1)) == 0) {
-            const int lo_lane = L, hi_lane = L + g;
+            const int lo_pt = L * P, hi_pt = (L + g) * P;
             const int s = (L + half) * P;
-            const int lo_pt = lo_lane * P, hi_pt = hi_lane * P;
-            int a = B.prev_vertex(s, lo_lane);
-            int b = B.next_vertex(s, hi_lane);
+            int a = sm.prv[s];
+            int b = sm.nxt[s];
             Pt Pa = B.pt(a), Ps = B.pt(s), Pb = B.pt(b);
             if (cross3(Pa, Ps, Pb) > 0.0) {
                 a = s;
                 b = s;  // convex at s: nothing removed
             } else {
-                // walk: a moves left while its turn towards b is not strictly
-                // left, b moves right likewise, until neither moves.  Every
-                // move removes a vertex, so the walk ends; the cap only guards.
+                // a moves left while its turn towards b is not strictly left,
+                // b moves right likewise, until neither moves.  Every move
+                // removes a vertex, so the walk ends; the cap only guards.
                 for (int pass = 0; pass < 2 * NT * P + 4; ++pass) {
                     bool moved = false;
                     while (a > lo_pt) {
-                        int a2 = B.prev_vertex(a, lo_lane);
-                        Pt P2 = B.pt(a2);
+                        const int a2 = sm.prv[a];
+                        const Pt P2 = B.pt(a2);
                         if (cross3(P2, Pa, Pb) <= 0.0) { a = a2; Pa = P2; moved = true; }
                         else break;
                     }
                     while (b < hi_pt) {
-                        int b2 = B.next_vertex(b, hi_lane);
-                        Pt P2 = B.pt(b2);
+                        const int b2 = sm.nxt[b];
+                        const Pt P2 = B.pt(b2);
                         if (cross3(Pa, Pb, P2) <= 0.0) { b = b2; Pb = P2; moved = true; }
                         else break;
                     }
                     if (!moved) break;
                 }
+                sm.nxt[a] = (int16_t)b;
+                sm.prv[b] = (int16_t)a;
             }
-            sm.blo[L] = a;
-            sm.bhi[L] = b;
+            sm.bra[(NT >> r) + (L >> (r + 1))] = (int16_t)a;
+            sm.brb[(NT >> r) + (L >> (r + 1))] = (int16_t)b;
         }
-        __syncthreads();
-        {
-            const int ldr = L & ~(g - 1);
-            const int a = sm.blo[ldr], b = sm.bhi[ldr];
-            int k0 = max(a + 1, base), k1 = min(b - 1, base + P - 1);
-            if (k0 <= k1) {
-                uint32_t clr = ((k1 - base == 31) ? 0xffffffffu : ((2u << (k1 - base)) - 1u)) &
-                               ~((1u << (k0 - base)) - 1u);
-                my &= ~clr;
-                sm.mask[L] = my;
-            }
-            unsigned long long bal = __ballot(my != 0u);
-            if ((L & 31) == 0) sm.occ[L >> 5] = (uint32_t)(bal >> (L & 32));
-        }
-        __syncthreads();
+        if (g < 64) wave_sync();
+        else __syncthreads();
     }
+    if (NT <= 64) __syncthreads();
+    // ---- clear the bits of vertices strictly inside any bridge of this
+    // thread's groups
+    for (int r = 0; r < R; ++r) {
+        const int i = (NT >> r) + (L >> (r + 1));
+        const int a = sm.bra[i], b = sm.brb[i];
+        const int k0 = max(a + 1, base), k1 = min(b - 1, base + P - 1);
+        if (k0 <= k1) {
+            const uint32_t clr = ((k1 - base == 31) ? 0xffffffffu : ((2u << (k1 - base)) - 1u)) &
+                                 ~((1u << (k0 - base)) - 1u);
+            my &= ~clr;
+        }
+    }
+    sm.mask[L] = my;
+    __syncthreads();
 }
 
 // ----------------------------------------------------------------------------
@@ -425,383 +415,24 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
         bits &= bits - 1u;
         int k = base + b;
         ws.slot_idx[slot + rank] = (uint16_t)min(k, len);
-        ws.slot_S[slot + rank] = sm.S[k];
-        if (WT) ws.slot_W[slot + rank] = sm.W[k];
+        ws.slot_S[slot + rank] = sm.S[sk<P>(k)];
+        if (WT) ws.slot_W[slot + rank] = sm.W[sk<P>(k)];
         const int e = wslot(rank);
-        if (e >= 0) wr->v[e] = make_double2(sm.S[k], WT ? sm.W[k] : (double)min(k, len));
+        if (e >= 0) wr->v[e] = make_double2(sm.S[sk<P>(k)], WT ? sm.W[sk<P>(k)] : (double)min(k, len));
         ++rank;
     }
     if (L == NT - 1) {
         // the chunk's last point (point len; padding repeats it) ends the hull
         ws.slot_idx[slot + total] = (uint16_t)len;
-        ws.slot_S[slot + total] = sm.S[C];
-        if (WT) ws.slot_W[slot + total] = sm.W[C];
-        wr->v[wslot(total)] = make_double2(sm.S[C], WT ? sm.W[C] : (double)len);
+        ws.slot_S[slot + total] = sm.S[sk<P>(C)];
+        if (WT) ws.slot_W[slot + total] = sm.W[sk<P>(C)];
+        wr->v[wslot(total)] = make_double2(sm.S[sk<P>(C)], WT ? sm.W[sk<P>(C)] : (double)len);
         wr->h = h;
         ws.hull_cnt[gid] = h;
-        ws.tot_S[gid] = sm.S[C];
-        if (WT) ws.tot_W[gid] = sm.W[C];
+        ws.tot_S[gid] = sm.S[sk<P>(C)];
+        if (WT) ws.tot_W[gid] = sm.W[sk<P>(C)];
         ws.chunk_flag[gid] = sm.flag;
     }
-}
-
-// ----------------------------------------------------------------------------
-// Long rows, phase 2: the merge tree over segment lists (paper section 3.3,
-// Algorithm 1, Definition 4.3, Theorem 4.4), one workgroup per row, a thread
-// per merge, every level in one launch.  Then the per-chunk reconstruction
-// records (section 3.4, Corollary 4.5).
-// ----------------------------------------------------------------------------
-// Bridge of the neighbouring lists L and R (Algorithm 1; Lemma 4.2): A is the
-// last vertex of L that stays, B the first vertex of R that stays.  In the
-// convex case A is the shared point s (kept once, in L) and B its successor.
-struct Bridge {
-    Cur A;
-    Cur B;
-};
-
-// Tests the chain at the shared point s.  Returns true when it is convex (the
-// bridge is then {A, B} as set); otherwise A, B are s's two neighbours, where
-// the walk starts.
-__device__ __forceinline__ bool bridge_start(const RowView X, const List Lq, const List Rq,
-                                             int jr, Cur& A, Cur& B) {
-    Cur sL = Lq.last();
-    Cur sR = Rq.first();
-    Pt Ps = Rq.pt(X, sR, jr);
-    A = Lq.prev(sL);  // every node has at least its two end points
-    B = Rq.next(sR);
-    Pt PA = Lq.pt(X, A, jr), PB = Rq.pt(X, B, jr);
-    if (cross3(PA, Ps, PB) > 0.0) {
-        A = sL;
-        return true;
-    }
-    return false;
-}
-
-// The walk of Lemma 4.2 by one thread: A moves left while its turn towards B is
-// not strictly left, B moves right likewise, until neither moves.  Returns
-// false if it gives up after `cap` steps (A, B then hold where it stopped; a
-// resumed walk reaches the same bridge).
-__device__ __forceinline__ bool walk_thread(const RowView X, const List Lq, const List Rq, int jr, Cur& A,
-                            Cur& B, int cap) {
-    Pt PA = Lq.pt(X, A, jr), PB = Rq.pt(X, B, jr);
-    int steps = 0;
-    for (;;) {
-        bool moved = false;
-        while (!Lq.is_first(A) && steps < cap) {
-            Cur A2 = Lq.prev(A);
-            Pt P2 = Lq.pt(X, A2, jr);
-            if (cross3(P2, PA, PB) <= 0.0) { A = A2; PA = P2; moved = true; ++steps; }
-            else break;
-        }
-        while (!Rq.is_last(B) && steps < cap) {
-            Cur B2 = Rq.next(B);
-            Pt P2 = Rq.pt(X, B2, jr);
-            if (cross3(PA, PB, P2) <= 0.0) { B = B2; PB = P2; moved = true; ++steps; }
-            else break;
-        }
-        if (!moved) return true;
-        if (steps >= cap) return false;
-    }
-}
-
-// Nested bisection (paper section 3.3, Theorem 5.2): A is the first vertex of L
-// whose successor does not lie below A's tangent line to R; B is where that
-// tangent touches R.  Used when a walk gives up.
-__device__ __noinline__ Bridge bisect_bridge(const RowView X, const List Lq, const List Rq, int jr) {
-    const Cur sL = Lq.last();
-    const Cur sR = Rq.first();
-    const Cur A0 = Lq.prev(sL);
-    const Cur B0 = Rq.next(sR);
-    const Cur RL = Rq.last();
-    auto tangent = [&](Pt Pa) -> Cur {
-        return find_first(Rq, B0, RL, [&](Cur r) -> bool {
-            if (Rq.is_last(r)) return true;
-            Pt Pr = Rq.pt(X, r, jr);
-            Pt Pn = Rq.pt(X, Rq.next(r), jr);
-            return cross3(Pa, Pr, Pn) > 0.0;
-        });
-    };
-    Cur A = find_first(Lq, Lq.first(), A0, [&](Cur c) -> bool {
-        if (c.seg == A0.seg && c.pos == A0.pos) return true;
-        Pt Pc = Lq.pt(X, c, jr);
-        Cur t = tangent(Pc);
-        Pt Pt_ = Rq.pt(X, t, jr);
-        Pt Pn = Lq.pt(X, Lq.next(c), jr);
-        return cross3(Pc, Pt_, Pn) >= 0.0;
-    });
-    Cur B = tangent(Lq.pt(X, A, jr));
-    return Bridge{A, B};
-}
-
-// For the 64 lanes of a wave: the vertex `lane` positions before (dir < 0) or
-// after (dir > 0) cursor C along the list, or valid = false past its end.
-// Every lane of the wave must call it with the same C and dir.
-__device__ __forceinline__ Cur wave_offset(const List Lq, Cur C, int dir, int lane, bool& valid) {
-    const int sj = C.seg + dir * lane;
-    int cnt = 0;
-    if (sj >= 0 && sj < Lq.n) {
-        uint2 d = Lq.d[sj];
-        if (lane == 0) cnt = dir < 0 ? C.pos - dlo(d) + 1 : dhi(d) - C.pos + 1;
-        else cnt = dhi(d) - dlo(d) + 1;
-    }
-    int cum = cnt;
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-        int t = __shfl_up(cum, k);
-        if (lane >= k) cum += t;
-    }
-    const int total = __shfl(cum, 63);
-    valid = lane < total;
-    // j = number of segments whose cumulative count is <= lane
-    int j = 0;
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) {
-        int c = __shfl(cum, j + k - 1);
-        if (c <= lane) j += k;
-    }
-    int before = __shfl(cum, j > 0 ? j - 1 : 0);
-    if (j == 0) before = 0;
-    if (!valid) return C;
-    const int seg = C.seg + dir * j;
-    const uint2 d = Lq.d[seg];
-    const int top = (j == 0) ? C.pos : (dir < 0 ? dhi(d) : dlo(d));
-    return Cur{seg, top + dir * (lane - before)};
-}
-
-__device__ __forceinline__ Pt shfl_down_pt(Pt p, int k) {
-    return Pt{__shfl_down(p.w, k), __shfl_down(p.s, k)};
-}
-__device__ __forceinline__ Cur bcast_cur(Cur c, int src) {
-    return Cur{__shfl(c.seg, src), __shfl(c.pos, src)};
-}
-
-// The same walk by a whole wave: each step tests the next 63 candidates at
-// once (the pages' warp-per-merge search, section 3.3, on 64 lanes).  The
-// candidate where a sequential walk would stop is the first lane whose test
-// holds.  Returns false if it gives up after `cap` steps.
-__device__ __forceinline__ bool walk_wave(const RowView X, const List Lq, const List Rq, int jr, Cur& A, Cur& B,
-                          int cap) {
-    const int lane = threadIdx.x & 63;
-    int steps = 0;
-    for (;;) {
-        bool moved = false;
-        // A moves left
-        for (;;) {
-            Pt PB = Rq.pt(X, B, jr);
-            bool valid;
-            Cur v = wave_offset(Lq, A, -1, lane, valid);
-            Pt Pv = valid ? Lq.pt(X, v, jr) : Pt{0.0, 0.0};
-            Pt Pu = shfl_down_pt(Pv, 1);
-            bool vnext = __shfl_down((int)valid, 1) != 0;
-            bool stop = valid && lane < 63 && (!vnext || cross3(Pu, Pv, PB) > 0.0);
-            unsigned long long bal = __ballot(stop);
-            if (bal) {
-                int i = __ffsll((long long)bal) - 1;
-                if (i > 0) moved = true;
-                A = bcast_cur(v, i);
-                break;
-            }
-            A = bcast_cur(v, 63);
-            moved = true;
-            if (++steps >= cap) return false;
-        }
-        // B moves right
-        for (;;) {
-            Pt PA = Lq.pt(X, A, jr);
-            bool valid;
-            Cur v = wave_offset(Rq, B, +1, lane, valid);
-            Pt Pv = valid ? Rq.pt(X, v, jr) : Pt{0.0, 0.0};
-            Pt Pn = shfl_down_pt(Pv, 1);
-            bool vnext = __shfl_down((int)valid, 1) != 0;
-            bool stop = valid && lane < 63 && (!vnext || cross3(PA, Pv, Pn) > 0.0);
-            unsigned long long bal = __ballot(stop);
-            if (bal) {
-                int i = __ffsll((long long)bal) - 1;
-                if (i > 0) moved = true;
-                B = bcast_cur(v, i);
-                break;
-            }
-            B = bcast_cur(v, 63);
-            moved = true;
-            if (++steps >= cap) return false;
-        }
-        if (!moved) return true;
-    }
-}
-
-// Writes the cut of one merge: L ends at A, R starts at B; records what the
-// descriptor move needs.
-__device__ __forceinline__ void apply_cut(uint2* D, int32_t* CNT, int2* MI, int k, int a, int b,
-                                          int nR, Bridge br) {
-    uint2 dl = D[a + br.A.seg];
-    D[a + br.A.seg] = mkdesc(dchunk(dl), dlo(dl), br.A.pos);
-    uint2 dr = D[b + br.B.seg];
-    D[b + br.B.seg] = mkdesc(dchunk(dr), br.B.pos, dhi(dr));
-    MI[k] = make_int2(br.A.seg + 1, br.B.seg);
-    CNT[a] = br.A.seg + 1 + (nR - br.B.seg);
-}
-
-// One workgroup per row runs every level of the merge tree.  Segment lists
-// live in LDS when the row has at most kMergeLdsMax chunks (else in the
-// workspace).  Per level: one thread per merge finds its bridge and cuts the two
-// boundary segments in place; then teams of threads move each right list's
-// remaining descriptors down behind the left list's (through a scratch copy,
-// since the two ranges may overlap).
-template <bool WT, bool INLDS>
-__global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
-    constexpr int NT = kMergeNT;
-    extern __shared__ uint2 dyn_lds[];
-    __shared__ double red[NT / 64 + 1];
-    __shared__ int ired[NT / 64 + 1];
-    __shared__ int sflag;
-    __shared__ int s_nhard;
-    __shared__ int4 s_hard[kHardCap];
-    constexpr int NW = NT / 64;
-    const int64_t row = blockIdx.x;
-    const int64_t rb = row * m;
-    const int tid = threadIdx.x;
-    const int wid = tid >> 6, wlane = tid & 63;
-
-    uint2* D;
-    uint2* SCR;
-    int32_t* CNT;
-    int2* MI;
-    int32_t* HC;
-    double* STS;
-    double* STW;
-    if (INLDS) {
-        D = dyn_lds;
-        SCR = D + m;
-        MI = reinterpret_cast<int2*>(SCR + m);
-        STS = reinterpret_cast<double*>(MI + (m / 2 + 1));
-        STW = STS + m;  // used when weighted
-        CNT = reinterpret_cast<int32_t*>(STW + (WT ? m : 0));
-        HC = CNT + m;
-    } else {
-        D = ws.desc + rb;
-        SCR = ws.desc_scr + rb;
-        CNT = ws.node_cnt + rb;
-        MI = ws.merge_info + rb;
-        HC = ws.hull_cnt + rb;
-        STS = ws.st_S + rb;
-        STW = WT ? ws.st_W + rb : nullptr;
-    }
-
-    // ---- row flags, chunk starts (exclusive scan of the chunk totals)
-    if (tid == 0) sflag = 0;
-    __syncthreads();
-    int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
-    if (f) atomicOr(&sflag, f);
-    double carryS = 0.0, carryW = 0.0;
-    for (int t0 = 0; t0 < m; t0 += NT) {
-        int j = t0 + tid;
-        double vs = j < m ? ws.tot_S[rb + j] : 0.0;
-        double tot;
-        double xs = wg_excl_scan<NT>(vs, red, &tot);
-        if (j < m) STS[j] = carryS + xs;
-        carryS += tot;
-        if (WT) {
-            double vw = j < m ? ws.tot_W[rb + j] : 0.0;
-            double xw = wg_excl_scan<NT>(vw, red, &tot);
-            if (j < m) STW[j] = carryW + xw;
-            carryW += tot;
-        }
-    }
-    for (int j = tid; j < m; j += NT) {
-        const int h = ws.hull_cnt[rb + j];
-        if (INLDS) HC[j] = h;
-        D[j] = mkdesc(j, 0, h - 1);
-        CNT[j] = 1;
-    }
-    // warm this XCD's L2 with the compact hull ends of the whole row
-    {
-        const double2* wv = reinterpret_cast<const double2*>(ws.win + rb);
-        const int nv2 = m * (int)(sizeof(WinRec) / sizeof(double2));
-        double acc = 0.0;
-        for (int i = tid; i < nv2; i += NT) acc += wv[i].x;
-        keep(acc);
-    }
-    __syncthreads();
-    if (tid == 0) ws.row_flag[row] = sflag;
-
-    const size_t sl = (size_t)rb * (kChunk + 1);
-    RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
-              STS, WT ? STW : nullptr, WT};
-
-    // ---- the merge tree, level by level
-    for (int span = 1; span < m; span <<= 1) {
-        const int nm = (m - span + 2 * span - 1) / (2 * span);
-        if (nm > NW) {
-            // many merges: a thread each; walks that run long go to the waves
-            if (tid == 0) s_nhard = 0;
-            __syncthreads();
-            for (int k = tid; k < nm; k += NT) {
-                const int a = 2 * k * span, b = a + span;
-                List Lq{D + a, CNT[a]};
-                List Rq{D + b, CNT[b]};
-                Bridge br;
-                if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
-                    !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
-                    int h = atomicAdd(&s_nhard, 1);
-                    if (h < kHardCap) {
-                        s_hard[h] = make_int4(k, br.A.seg, br.A.pos, (br.B.seg << 16) | br.B.pos);
-                        continue;
-                    }
-                    br = bisect_bridge(X, Lq, Rq, b);
-                }
-                apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-            __syncthreads();
-            const int nh = min(s_nhard, kHardCap);
-            for (int h = wid; h < nh; h += NW) {
-                const int4 hk = s_hard[h];
-                const int k = hk.x, a = 2 * k * span, b = a + span;
-                List Lq{D + a, CNT[a]};
-                List Rq{D + b, CNT[b]};
-                Bridge br{Cur{hk.y, hk.z}, Cur{hk.w >> 16, hk.w & 0xffff}};
-                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                    br = bisect_bridge(X, Lq, Rq, b);
-                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-        } else {
-            // few merges: a wave each
-            for (int k = wid; k < nm; k += NW) {
-                const int a = 2 * k * span, b = a + span;
-                List Lq{D + a, CNT[a]};
-                List Rq{D + b, CNT[b]};
-                Bridge br;
-                if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
-                    if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                        br = bisect_bridge(X, Lq, Rq, b);
-                }
-                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-        }
-        __syncthreads();
-        // move the right lists' tails: teams of ts threads per merge
-        int ts = NT / nm;
-        ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
-        const int teams = NT / ts;
-        const int lane = tid & (ts - 1);
-        for (int k = tid / ts; k < nm; k += teams) {
-            const int b = (2 * k + 1) * span;
-            const int rs = MI[k].y;
-            const int nr = CNT[b] - rs;
-            for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
-        }
-        __syncthreads();
-        for (int k = tid / ts; k < nm; k += teams) {
-            const int a = 2 * k * span, b = a + span;
-            const int nl = MI[k].x;
-            const int nr = CNT[b] - MI[k].y;
-            for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
-        }
-        __syncthreads();
-    }
-
-    // ---- reconstruction records (Corollary 4.5)
-    write_records<NT>(X, D, CNT[0], m, ws.vb + rb, ws.rec + rb, ired);
 }
 
 // ----------------------------------------------------------------------------
@@ -893,13 +524,6 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
     }
 }
 
-size_t merge_lds_bytes(int m, bool weighted) {
-    // D, SCR (8 B each), MI (8 B per merge), STS (8 B), STW (8 B, weighted),
-    // CNT, HC (4 B each)
-    return (size_t)m * 16 + (size_t)(m / 2 + 1) * 8 + (size_t)m * (weighted ? 16 : 8) +
-           (size_t)m * 8;
-}
-
 template <int NT, int P>
 hipError_t launch_short_t(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                           float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {
@@ -924,40 +548,6 @@ hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n,
     if (n <= 512) return launch_short_t<64, 8>(y, w, rows, n, sign, out, block_id, row_flag, st);
     if (n <= 1024) return launch_short_t<64, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
     return launch_short_t<256, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
-}
-
-// The merge phase over segment lists: one workgroup per row, lists in LDS when
-// they fit.
-hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st) {
-    const bool wt = sh.weighted;
-    timed_begin(kPhaseMerge, st);
-    if (sh.m <= kMergeLdsMax) {
-        const size_t lds = merge_lds_bytes(sh.m, wt);
-        static bool attr_set = false;
-        if (!attr_set) {
-            const int maxb = (int)merge_lds_bytes(kMergeLdsMax, true);
-            (void)hipFuncSetAttribute((const void*)k_merge_rows<true, true>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-            (void)hipFuncSetAttribute((const void*)k_merge_rows<false, true>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-            attr_set = true;
-        }
-        if (wt)
-            hipLaunchKernelGGL((k_merge_rows<true, true>), dim3((unsigned)sh.rows), dim3(kMergeNT), lds,
-                               st, sh.m, ws);
-        else
-            hipLaunchKernelGGL((k_merge_rows<false, true>), dim3((unsigned)sh.rows), dim3(kMergeNT),
-                               lds, st, sh.m, ws);
-    } else {
-        if (wt)
-            hipLaunchKernelGGL((k_merge_rows<true, false>), dim3((unsigned)sh.rows), dim3(kMergeNT), 0,
-                               st, sh.m, ws);
-        else
-            hipLaunchKernelGGL((k_merge_rows<false, false>), dim3((unsigned)sh.rows), dim3(kMergeNT),
-                               0, st, sh.m, ws);
-    }
-    timed_end(st);
-    return hipGetLastError();
 }
 
 hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,

@@ -18,6 +18,10 @@ constexpr int kShortMax = 4096;
 constexpr int kMergeNT = 1024;
 constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
 constexpr int kWinK = 8;            // hull vertices kept at each end of a chunk's window
+constexpr int kGroup = 64;          // chunks per group of the first merge stage
+constexpr int kGroupNT = 256;
+constexpr int kTopNT = 1024;
+constexpr int kTopMax = 256;        // groups per row the second stage keeps in LDS
 constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed to a wave
 constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
 constexpr int kHardCap = 256;     // merges per level a wave may take over
@@ -52,6 +56,16 @@ struct WinRec {
     double2 v[2 * kWinK];
 };
 
+// The same for the hull of a group of kGroup chunks (first merge stage): its
+// vertex count, the number of segments in its list, and the (S, W) of its
+// first and last kWinK vertices relative to the group's first point.
+struct GroupWin {
+    int32_t h;
+    int32_t nseg;
+    int32_t pad[2];
+    double2 v[2 * kWinK];
+};
+
 // Device pointers of the long-row workspace (see plan_long in iso_api.hip).
 struct LongWs {
     int32_t* chunk_flag;  // [R*m]
@@ -67,7 +81,11 @@ struct LongWs {
     uint2* desc;          // [R*m] segment descriptors (chunk, lo | hi << 16)
     int32_t* node_cnt;    // [R*m] segments in the list stored from this slot
     int32_t* vb;          // [R*m] scratch: vertex prefix over the root list
-    uint2* desc_scr;      // [R*m] scratch for descriptor moves (lists in the workspace)
+    uint2* desc_scr;      // [R*m] scratch for descriptor moves; the two-stage merge's root list
+    GroupWin* gwin;       // [R*ng] group hull ends (ng = groups per row)
+    double2* gtot;        // [R*ng] group totals (S, W)
+    double2* cst;         // [R*m] chunk starts relative to their group's start
+    int32_t* gpre;        // [R*m] vertices before each segment of a group's list
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
@@ -92,7 +110,7 @@ struct LongShape {
 
 // Phases of the launch timing (the ISO_PHASE_* values of iso.h).
 constexpr int kPhaseShort = 0, kPhaseChunk = 1, kPhaseMerge = 2, kPhaseExpand = 3,
-              kPhaseCopyBridge = 4, kPhaseCopyMove = 5;
+              kPhaseCopyBridge = 4, kPhaseCopyMove = 5, kPhaseMergeTop = 6;
 
 // Launch timing for benchmarks (iso_timing_enable / iso_timing_read): when
 // enabled, timed_begin records an event before a launch and timed_end one
@@ -102,6 +120,10 @@ void timed_end(hipStream_t st);
 
 hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                         float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
+
+// The merge phase over segment lists (iso_merge.hip); leaves the
+// reconstruction records in ws.rec.
+hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
 
 // The merge phase of the vertex-copying control (iso_copy.hip); leaves the
 // reconstruction records in ws.rec like the segment-list merge.

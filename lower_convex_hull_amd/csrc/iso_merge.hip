@@ -1,0 +1,588 @@
+// The merge phase of long rows: chunk hulls merged up a tree whose nodes are
+// lists of segments of chunk hulls, at most one per chunk (paper "Merge Hulls
+// Without Copying Vertices: GPU Isotonic Regression", section 3.3, Algorithm 1,
+// Definition 4.3, Theorem 4.4), then the per-chunk reconstruction records
+// (section 3.4, Corollary 4.5).
+#include "iso_kernels.hpp"
+
+#include "iso_device.hpp"
+
+namespace iso {
+namespace {
+
+// One workgroup per row runs every level of the merge tree.  Segment lists
+// live in LDS when the row has at most kMergeLdsMax chunks (else in the
+// workspace).  Per level: one thread per merge finds its bridge and cuts the two
+// boundary segments in place; then teams of threads move each right list's
+// remaining descriptors down behind the left list's (through a scratch copy,
+// since the two ranges may overlap).
+template <bool WT, bool INLDS>
+__global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
+    constexpr int NT = kMergeNT;
+    extern __shared__ uint2 dyn_lds[];
+    __shared__ double red[NT / 64 + 1];
+    __shared__ int ired[NT / 64 + 1];
+    __shared__ int sflag;
+    __shared__ int s_nhard;
+    __shared__ int4 s_hard[kHardCap];
+    constexpr int NW = NT / 64;
+    const int64_t row = blockIdx.x;
+    const int64_t rb = row * m;
+    const int tid = threadIdx.x;
+    const int wid = tid >> 6, wlane = tid & 63;
+
+    uint2* D;
+    uint2* SCR;
+    int32_t* CNT;
+    int2* MI;
+    int32_t* HC;
+    double* STS;
+    double* STW;
+    if (INLDS) {
+        D = dyn_lds;
+        SCR = D + m;
+        MI = reinterpret_cast<int2*>(SCR + m);
+        STS = reinterpret_cast<double*>(MI + (m / 2 + 1));
+        STW = STS + m;  // used when weighted
+        CNT = reinterpret_cast<int32_t*>(STW + (WT ? m : 0));
+        HC = CNT + m;
+    } else {
+        D = ws.desc + rb;
+        SCR = ws.desc_scr + rb;
+        CNT = ws.node_cnt + rb;
+        MI = ws.merge_info + rb;
+        HC = ws.hull_cnt + rb;
+        STS = ws.st_S + rb;
+        STW = WT ? ws.st_W + rb : nullptr;
+    }
+
+    // ---- row flags, chunk starts (exclusive scan of the chunk totals)
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int f = 0;
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    if (f) atomicOr(&sflag, f);
+    double carryS = 0.0, carryW = 0.0;
+    for (int t0 = 0; t0 < m; t0 += NT) {
+        int j = t0 + tid;
+        double vs = j < m ? ws.tot_S[rb + j] : 0.0;
+        double tot;
+        double xs = wg_excl_scan<NT>(vs, red, &tot);
+        if (j < m) STS[j] = carryS + xs;
+        carryS += tot;
+        if (WT) {
+            double vw = j < m ? ws.tot_W[rb + j] : 0.0;
+            double xw = wg_excl_scan<NT>(vw, red, &tot);
+            if (j < m) STW[j] = carryW + xw;
+            carryW += tot;
+        }
+    }
+    for (int j = tid; j < m; j += NT) {
+        const int h = ws.hull_cnt[rb + j];
+        if (INLDS) HC[j] = h;
+        D[j] = mkdesc(j, 0, h - 1);
+        CNT[j] = 1;
+    }
+    // warm this XCD's L2 with the compact hull ends of the whole row
+    {
+        const double2* wv = reinterpret_cast<const double2*>(ws.win + rb);
+        const int nv2 = m * (int)(sizeof(WinRec) / sizeof(double2));
+        double acc = 0.0;
+        for (int i = tid; i < nv2; i += NT) acc += wv[i].x;
+        keep(acc);
+    }
+    __syncthreads();
+    if (tid == 0) ws.row_flag[row] = sflag;
+
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
+              STS, WT ? STW : nullptr, WT};
+
+    // ---- the merge tree, level by level
+    for (int span = 1; span < m; span <<= 1) {
+        const int nm = (m - span + 2 * span - 1) / (2 * span);
+        if (nm > NW) {
+            // many merges: a thread each; walks that run long go to the waves
+            if (tid == 0) s_nhard = 0;
+            __syncthreads();
+            for (int k = tid; k < nm; k += NT) {
+                const int a = 2 * k * span, b = a + span;
+                List<uint2> Lq{D + a, CNT[a]};
+                List<uint2> Rq{D + b, CNT[b]};
+                Bridge br;
+                if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
+                    !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
+                    int h = atomicAdd(&s_nhard, 1);
+                    if (h < kHardCap) {
+                        s_hard[h] = make_int4(k, br.A.seg, br.A.pos, (br.B.seg << 16) | br.B.pos);
+                        continue;
+                    }
+                    br = bisect_bridge(X, Lq, Rq, b);
+                }
+                apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+            __syncthreads();
+            const int nh = min(s_nhard, kHardCap);
+            for (int h = wid; h < nh; h += NW) {
+                const int4 hk = s_hard[h];
+                const int k = hk.x, a = 2 * k * span, b = a + span;
+                List<uint2> Lq{D + a, CNT[a]};
+                List<uint2> Rq{D + b, CNT[b]};
+                Bridge br{Cur{hk.y, hk.z}, Cur{hk.w >> 16, hk.w & 0xffff}};
+                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                    br = bisect_bridge(X, Lq, Rq, b);
+                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+        } else {
+            // few merges: a wave each
+            for (int k = wid; k < nm; k += NW) {
+                const int a = 2 * k * span, b = a + span;
+                List<uint2> Lq{D + a, CNT[a]};
+                List<uint2> Rq{D + b, CNT[b]};
+                Bridge br;
+                if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
+                    if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                        br = bisect_bridge(X, Lq, Rq, b);
+                }
+                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+            }
+        }
+        __syncthreads();
+        // move the right lists' tails: teams of ts threads per merge
+        int ts = NT / nm;
+        ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
+        const int teams = NT / ts;
+        const int lane = tid & (ts - 1);
+        for (int k = tid / ts; k < nm; k += teams) {
+            const int b = (2 * k + 1) * span;
+            const int rs = MI[k].y;
+            const int nr = CNT[b] - rs;
+            for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
+        }
+        __syncthreads();
+        for (int k = tid / ts; k < nm; k += teams) {
+            const int a = 2 * k * span, b = a + span;
+            const int nl = MI[k].x;
+            const int nr = CNT[b] - MI[k].y;
+            for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
+        }
+        __syncthreads();
+    }
+
+    // ---- reconstruction records (Corollary 4.5)
+    write_records<NT>(X, D, CNT[0], m, ws.vb + rb, ws.rec + rb, ired);
+}
+
+
+// ----------------------------------------------------------------------------
+// Two-stage merge.  Stage 1: one workgroup per group of kGroup consecutive
+// chunks merges their hulls (the tree's lower levels) with the chunk windows,
+// lists and starts in LDS.  Stage 2: one workgroup per row merges the group
+// hulls (the upper levels) with the group windows in LDS; a vertex outside a
+// group window is found through the group's segment list.  Every walk step
+// then reads LDS instead of a chain of cache misses.
+// ----------------------------------------------------------------------------
+
+// Runs one level of merges of the lists stored in D (slots a, a + span, ...):
+// a thread per merge when there are more merges than waves, handing walks that
+// run long to the waves; a wave per merge otherwise.  Then moves each right
+// list's kept descriptors down behind its left list's.
+template <int NT, class V, class DT>
+__device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* CNT, int2* MI, int m, int span,
+                            int* s_nhard, int4* s_hard, int hard_cap) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
+    const int nm = (m - span + 2 * span - 1) / (2 * span);
+    if (nm > NW) {
+        if (tid == 0) *s_nhard = 0;
+        __syncthreads();
+        for (int k = tid; k < nm; k += NT) {
+            const int a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br;
+            if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
+                !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
+                int h = atomicAdd(s_nhard, 1);
+                if (h < hard_cap) {
+                    s_hard[h] = make_int4(k, br.A.seg, br.A.pos, br.B.seg);
+                    MI[k] = make_int2(br.B.pos, 0);  // parked until the wave finishes it
+                    continue;
+                }
+                br = bisect_bridge(X, Lq, Rq, b);
+            }
+            apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+        __syncthreads();
+        const int nh = min(*s_nhard, hard_cap);
+        for (int h = wid; h < nh; h += NW) {
+            const int4 hk = s_hard[h];
+            const int k = hk.x, a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br{Cur{hk.y, hk.z}, Cur{hk.w, MI[k].x}};
+            if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                br = bisect_bridge(X, Lq, Rq, b);
+            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+    } else {
+        for (int k = wid; k < nm; k += NW) {
+            const int a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br;
+            if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
+                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
+                    br = bisect_bridge(X, Lq, Rq, b);
+            }
+            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+    }
+    __syncthreads();
+    int ts = NT / nm;
+    ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
+    const int teams = NT / ts;
+    const int lane = tid & (ts - 1);
+    for (int k = tid / ts; k < nm; k += teams) {
+        const int b = (2 * k + 1) * span;
+        const int rs = MI[k].y;
+        const int nr = CNT[b] - rs;
+        for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
+    }
+    __syncthreads();
+    for (int k = tid / ts; k < nm; k += teams) {
+        const int a = 2 * k * span, b = a + span;
+        const int nl = MI[k].x;
+        const int nr = CNT[b] - MI[k].y;
+        for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
+    }
+    __syncthreads();
+}
+
+// Vertices of group hulls for the second stage: position p of group g's hull,
+// relative to group gr's first point.
+struct GroupView {
+    const GroupWin* gw;  // group windows (LDS)
+    const int32_t* gh;   // group hull vertex counts (LDS)
+    const double* gS;    // group starts (LDS)
+    const double* gW;
+    const uint2* gdesc;  // group lists (chunk segments), stored from each group's first chunk
+    const int32_t* gpre; // vertices before each segment of a group list
+    const double2* cst;  // chunk starts relative to their group
+    RowView C;           // chunk hull vertices (chunk-relative)
+    bool weighted;
+
+    __device__ __forceinline__ Pt vtx(int g, int pos, int gr) const {
+        const int h = gh[g];
+        int e = pos;
+        if (h > 2 * kWinK && pos >= kWinK) e = pos >= h - kWinK ? kWinK + pos - (h - kWinK) : -1;
+        double s, w;
+        if (e >= 0) {
+            const double2 v = gw[g].v[e];
+            s = v.x;
+            w = v.y;
+        } else {
+            // the segment of the group's list that holds position pos
+            const int base = g * kGroup;
+            int lo = 0, hi = gw[g].nseg - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (gpre[base + mid] <= pos) lo = mid;
+                else hi = mid - 1;
+            }
+            const uint2 d = gdesc[base + lo];
+            const int j = dchunk(d);
+            const Pt v = C.vrel(j, dlo(d) + (pos - gpre[base + lo]));
+            const double2 c = cst[j];
+            s = c.x + v.s;
+            w = c.y + v.w;
+        }
+        Pt p;
+        p.s = (gS[g] - gS[gr]) + s;
+        p.w = (gW[g] - gW[gr]) + w;
+        return p;
+    }
+};
+
+template <bool WT>
+__global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
+    constexpr int NT = kGroupNT, G = kGroup;
+    __shared__ WinRec Wn[G];
+    __shared__ double lS[G], lW[G];
+    __shared__ int32_t HC[G], CNT[G], pre[G + 1];
+    __shared__ uint2 D[G], SCR[G];
+    __shared__ int2 MI[G / 2 + 1];
+    __shared__ int s_nhard;
+    __shared__ int4 s_hard[G / 2];
+    __shared__ int ired[NT / 64 + 1];
+    __shared__ int sflag;
+    const int64_t gid = blockIdx.x;
+    const int64_t row = gid / ng;
+    const int g = (int)(gid - row * ng);
+    const int64_t rb = row * m;
+    const int j0 = g * G, gc = min(G, m - j0);
+    const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
+
+    {
+        const double2* src = reinterpret_cast<const double2*>(ws.win + rb + j0);
+        double2* dst = reinterpret_cast<double2*>(Wn);
+        const int nv2 = gc * (int)(sizeof(WinRec) / sizeof(double2));
+        for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+    }
+    if (wid == 0) {
+        // chunk starts relative to the group: a scan of the chunk totals
+        double ts = wlane < gc ? ws.tot_S[rb + j0 + wlane] : 0.0;
+        double tw = (WT && wlane < gc) ? ws.tot_W[rb + j0 + wlane] : 0.0;
+        double is = ts, iw = tw;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            double us = __shfl_up(is, d), uw = __shfl_up(iw, d);
+            if (wlane >= d) { is += us; iw += uw; }
+        }
+        double es = __shfl_up(is, 1), ew = __shfl_up(iw, 1);
+        if (wlane == 0) { es = 0.0; ew = 0.0; }
+        if (!WT) ew = (double)wlane * kChunk;  // unit weights: W is the point index
+        if (wlane < gc) {
+            lS[wlane] = es;
+            lW[wlane] = ew;
+            ws.cst[rb + j0 + wlane] = make_double2(es, ew);
+        }
+        const double totS = __shfl(is, 63), totW = __shfl(iw, 63);
+        if (wlane == 0) ws.gtot[row * ng + g] = make_double2(totS, WT ? totW : 0.0);
+    }
+    __syncthreads();
+    for (int i = tid; i < gc; i += NT) {
+        HC[i] = Wn[i].h;
+        D[i] = mkdesc(i, 0, Wn[i].h - 1);
+        CNT[i] = 1;
+    }
+    __syncthreads();
+    const size_t sl = (size_t)(rb + j0) * (kChunk + 1);
+    const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT};
+    for (int span = 1; span < gc; span <<= 1)
+        merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
+
+    // ---- the group's list, its vertex prefix, and its window
+    const int nseg = CNT[0];
+    if (wid == 0) {
+        int v = 0;
+        if (wlane < nseg) v = dhi(D[wlane]) - dlo(D[wlane]) + 1;
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            int u = __shfl_up(x, d);
+            if (wlane >= d) x += u;
+        }
+        if (wlane < nseg) pre[wlane + 1] = x;
+        if (wlane == 0) pre[0] = 0;
+    }
+    __syncthreads();
+    const int hg = pre[nseg];
+    for (int i = tid; i < nseg; i += NT) {
+        const uint2 d = D[i];
+        ws.desc[rb + j0 + i] = mkdesc(j0 + dchunk(d), dlo(d), dhi(d));
+        ws.gpre[rb + j0 + i] = pre[i];
+    }
+    GroupWin* gwo = ws.gwin + row * ng + g;
+    const int nwin = min(hg, 2 * kWinK);
+    for (int t = tid; t < nwin; t += NT) {
+        const int r = (hg <= 2 * kWinK || t < kWinK) ? t : hg - 2 * kWinK + t;
+        int lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        const uint2 d = D[lo];
+        const Pt v = X.vtx(dchunk(d), dlo(d) + (r - pre[lo]), 0);
+        gwo->v[t] = make_double2(v.s, v.w);
+    }
+    if (tid == 0) {
+        gwo->h = hg;
+        gwo->nseg = nseg;
+    }
+    if (ng == 1) {
+        // the group is the whole row: its list is the root
+        if (tid == 0) sflag = 0;
+        __syncthreads();
+        int f = 0;
+        for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+        if (f) atomicOr(&sflag, f);
+        write_records<NT>(X, D, nseg, m, ws.vb + rb, ws.rec + rb, ired);
+        __syncthreads();
+        if (tid == 0) ws.row_flag[row] = sflag;
+    }
+}
+
+template <bool WT>
+__global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
+    constexpr int NT = kTopNT, G = kGroup;
+    extern __shared__ int4 top_lds[];
+    __shared__ double red[NT / 64 + 1];
+    __shared__ int ired[NT / 64 + 1];
+    __shared__ int s_nhard;
+    __shared__ int4 s_hard[kHardCap];
+    __shared__ int sflag;
+    const int64_t row = blockIdx.x;
+    const int64_t rb = row * m, gb = row * ng;
+    const int tid = threadIdx.x;
+    int4* D = top_lds;
+    int4* SCR = D + ng;
+    GroupWin* GW = reinterpret_cast<GroupWin*>(SCR + ng);
+    double* gS = reinterpret_cast<double*>(GW + ng);
+    double* gW = gS + ng;
+    int2* MI = reinterpret_cast<int2*>(gW + ng);
+    int32_t* CNT = reinterpret_cast<int32_t*>(MI + (ng / 2 + 1));
+    int32_t* GH = CNT + ng;
+
+    {
+        const double2* src = reinterpret_cast<const double2*>(ws.gwin + gb);
+        double2* dst = reinterpret_cast<double2*>(GW);
+        const int nv2 = ng * (int)(sizeof(GroupWin) / sizeof(double2));
+        for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+    }
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int f = 0;
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    if (f) atomicOr(&sflag, f);
+    double cS = 0.0, cW = 0.0;
+    for (int t0 = 0; t0 < ng; t0 += NT) {
+        const int g = t0 + tid;
+        const double2 gt = g < ng ? ws.gtot[gb + g] : make_double2(0.0, 0.0);
+        double tot;
+        const double xs = wg_excl_scan<NT>(gt.x, red, &tot);
+        if (g < ng) gS[g] = cS + xs;
+        cS += tot;
+        if (WT) {
+            const double xw = wg_excl_scan<NT>(gt.y, red, &tot);
+            if (g < ng) gW[g] = cW + xw;
+            cW += tot;
+        } else if (g < ng) {
+            gW[g] = (double)((int64_t)g * G * kChunk);
+        }
+    }
+    for (int g = tid; g < ng; g += NT) {
+        GH[g] = GW[g].h;
+        D[g] = make_int4(g, 0, GW[g].h - 1, 0);
+        CNT[g] = 1;
+    }
+    __syncthreads();
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                     ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+    const GroupView X{GW, GH, gS, gW, ws.desc + rb, ws.gpre + rb, ws.cst + rb, Cv, WT};
+    for (int span = 1; span < ng; span <<= 1)
+        merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
+
+    // ---- the root list over groups, as segments of chunk hulls
+    const int nr2 = CNT[0];
+    uint2* R = ws.desc_scr + rb;
+    int carry = 0;
+    for (int t0 = 0; t0 < nr2; t0 += NT) {
+        const int t = t0 + tid;
+        int ilo = 0, ihi = 0, g = 0, lo = 0, hi = 0;
+        if (t < nr2) {
+            const int4 d = D[t];
+            g = d.x;
+            lo = d.y;
+            hi = d.z;
+            const int base = g * G, ns = GW[g].nseg;
+            auto seg_of = [&](int p) {
+                int a = 0, b = ns - 1;
+                while (a < b) {
+                    const int mid = (a + b + 1) >> 1;
+                    if (ws.gpre[rb + base + mid] <= p) a = mid;
+                    else b = mid - 1;
+                }
+                return a;
+            };
+            ilo = seg_of(lo);
+            ihi = seg_of(hi);
+        }
+        int tot;
+        const int x = wg_excl_scan_int<NT>(t < nr2 ? ihi - ilo + 1 : 0, ired, &tot);
+        if (t < nr2) {
+            const int base = g * G;
+            for (int i = ilo; i <= ihi; ++i) {
+                const uint2 d = ws.desc[rb + base + i];
+                const int pre_i = ws.gpre[rb + base + i];
+                const int a = i == ilo ? dlo(d) + (lo - pre_i) : dlo(d);
+                const int b = i == ihi ? dlo(d) + (hi - pre_i) : dhi(d);
+                R[carry + x + (i - ilo)] = mkdesc(dchunk(d), a, b);
+            }
+        }
+        carry += tot;
+    }
+    // chunk starts of the row: group start plus the chunk's start in its group
+    for (int j = tid; j < m; j += NT) {
+        const double2 c = ws.cst[rb + j];
+        ws.st_S[rb + j] = gS[j / G] + c.x;
+        if (WT) ws.st_W[rb + j] = gW[j / G] + c.y;
+    }
+    __syncthreads();
+    if (tid == 0) ws.row_flag[row] = sflag;
+    write_records<NT>(Cv, R, carry, m, ws.vb + rb, ws.rec + rb, ired);
+}
+
+size_t top_lds_bytes(int ng) {
+    // D, SCR (16 B each), GW, gS, gW (8 B each), MI (8 B per merge), CNT, GH (4 B each)
+    return (size_t)ng * (32 + sizeof(GroupWin) + 16 + 8) + (size_t)(ng / 2 + 1) * 8;
+}
+
+}  // namespace
+
+size_t merge_lds_bytes(int m, bool weighted) {
+    // D, SCR (8 B each), MI (8 B per merge), STS (8 B), STW (8 B, weighted),
+    // CNT, HC (4 B each)
+    return (size_t)m * 16 + (size_t)(m / 2 + 1) * 8 + (size_t)m * (weighted ? 16 : 8) +
+           (size_t)m * 8;
+}
+
+// The merge phase over segment lists: one workgroup per row, lists in LDS when
+// they fit.
+hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st) {
+    const bool wt = sh.weighted;
+    const int ng = (sh.m + kGroup - 1) / kGroup;
+    const unsigned R = (unsigned)sh.rows;
+    if (ng <= kTopMax) {
+        timed_begin(kPhaseMerge, st);
+        if (wt)
+            hipLaunchKernelGGL(k_group_merge<true>, dim3(R * (unsigned)ng), dim3(kGroupNT), 0, st, sh.m,
+                               ng, ws);
+        else
+            hipLaunchKernelGGL(k_group_merge<false>, dim3(R * (unsigned)ng), dim3(kGroupNT), 0, st, sh.m,
+                               ng, ws);
+        timed_end(st);
+        if (ng > 1) {
+            const size_t lds = top_lds_bytes(ng);
+            static bool attr_set = false;
+            if (!attr_set) {
+                const int maxb = (int)top_lds_bytes(kTopMax);
+                (void)hipFuncSetAttribute((const void*)k_top_merge<true>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
+                (void)hipFuncSetAttribute((const void*)k_top_merge<false>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
+                attr_set = true;
+            }
+            timed_begin(kPhaseMergeTop, st);
+            if (wt)
+                hipLaunchKernelGGL(k_top_merge<true>, dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+            else
+                hipLaunchKernelGGL(k_top_merge<false>, dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+            timed_end(st);
+        }
+        return hipGetLastError();
+    }
+    // very long rows: one workgroup per row merges every level, lists in the
+    // workspace
+    timed_begin(kPhaseMerge, st);
+    if (wt)
+        hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+    else
+        hipLaunchKernelGGL((k_merge_rows<false, false>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+    timed_end(st);
+    return hipGetLastError();
+}
+
+}  // namespace iso
