@@ -57,9 +57,10 @@ def parse():
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("iso_kernels.hip", "iso_kernels.hpp", "iso_api.hip"):
-        with open(os.path.join(ROOT, "lower_convex_hull_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    src = os.path.join(ROOT, "lower_convex_hull_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
