@@ -16,8 +16,17 @@ struct Pt {
 // means b lies strictly below the chord from a to c (a strict left turn), so b
 // is a hull vertex of {a, b, c}; <= 0 means b is on or above the chord and is
 // dropped (collinear middle points are not vertices, paper section 2.1).
+// The two products are rounded separately (no fused multiply-add), so a
+// repeated point or an exactly collinear triple gives exactly 0.
 __device__ __forceinline__ double cross3(Pt a, Pt b, Pt c) {
-    return (b.w - a.w) * (c.s - a.s) - (b.s - a.s) * (c.w - a.w);
+    return __dmul_rn(b.w - a.w, c.s - a.s) - __dmul_rn(b.s - a.s, c.w - a.w);
+}
+
+// Makes one lane's LDS writes visible to the other lanes of its wave and keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
 }
 
 __device__ __forceinline__ int msb32(uint32_t x) { return 31 - __clz((int)x); }
@@ -447,6 +456,254 @@ __device__ void write_records(const RowView X, const uint2* D, int nroot, int m,
             // always holds the row's first point)
             uint2 p = D[i - 1];
             Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
+            rc.lo = -1;
+            rc.hi = -1;
+            rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+            rc.slope_out = rc.slope_in;
+        }
+        rec[j] = rc;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Compact hull arrays for the merge fast paths (hulls short enough that every
+// vertex is in the window records): entry i holds (S, W) relative to a common
+// origin and a tag naming the vertex's chunk and its position in that chunk's
+// hull.  A node's hull sits at the start of its region and is merged with its
+// neighbour's as in the chunk kernel: bridge, then the right array's kept
+// entries are moved down behind the left array's kept ones.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int mktag(int j, int pos) { return (j << kTagShift) | pos; }
+__device__ __forceinline__ int tchunk(int t) { return t >> kTagShift; }
+__device__ __forceinline__ int tpos(int t) { return t & ((1 << kTagShift) - 1); }
+
+struct Arr {
+    double* S;
+    double* W;
+    int32_t* tag;
+    __device__ __forceinline__ Pt pt(int i) const { return Pt{W[i], S[i]}; }
+};
+
+// Bridge of the neighbouring compact hulls L = entries l0 .. l0+cL-1 and
+// R = r0 .. r0+cR-1 (L's last vertex is R's first), found by a team of T lanes
+// of one wave (lanes lane0 .. lane0+T-1; x is the lane's place in the team).
+// The walk of Lemma 4.2 is kept, but each of its steps tests the next T
+// candidates at once and a ballot finds where a lane-by-lane walk would stop.
+// Returns (A, B): L keeps entries 0..A, R keeps B..cR-1.  Every lane of the
+// wave calls it (the loops are wave-uniform); act marks lanes whose team has a
+// merge.
+__device__ __forceinline__ int2 team_bridge(const Arr& ar, int l0, int cL, int r0, int cR, int x,
+                                            int T, int lane0, bool act) {
+    const uint64_t tm = (T == 64) ? ~0ull : (((1ull << T) - 1ull) << lane0);
+    int A = cL - 2, B = 1;
+    bool run = act;
+    if (act) {
+        const Pt PA = ar.pt(l0 + A), Ps = ar.pt(r0), PB = ar.pt(r0 + 1);
+        if (cross3(PA, Ps, PB) > 0.0) {
+            A = cL - 1;  // convex at the shared point: kept once, in L
+            run = false;
+        }
+    }
+    for (;;) {
+        if (__ballot(run) == 0) break;
+        bool moved = false;
+        // A moves left while its turn towards B is not strictly left
+        {
+            const Pt PB = run ? ar.pt(r0 + B) : Pt{0.0, 0.0};
+            bool go = run;
+            for (;;) {
+                if (__ballot(go) == 0) break;
+                bool stop = false;
+                if (go) {
+                    const int c = A - x;
+                    stop = c <= 0 || cross3(ar.pt(l0 + c - 1), ar.pt(l0 + c), PB) > 0.0;
+                }
+                const uint64_t bal = __ballot(go && stop) & tm;
+                if (go) {
+                    const int xs = bal ? (__ffsll((long long)bal) - 1 - lane0) : T;
+                    A -= xs;
+                    if (xs > 0) moved = true;
+                    if (xs < T) go = false;
+                }
+            }
+        }
+        // B moves right likewise
+        {
+            const Pt PA = run ? ar.pt(l0 + A) : Pt{0.0, 0.0};
+            bool go = run;
+            for (;;) {
+                if (__ballot(go) == 0) break;
+                bool stop = false;
+                if (go) {
+                    const int c = B + x;
+                    stop = c >= cR - 1 || cross3(PA, ar.pt(r0 + c), ar.pt(r0 + c + 1)) > 0.0;
+                }
+                const uint64_t bal = __ballot(go && stop) & tm;
+                if (go) {
+                    const int xs = bal ? (__ffsll((long long)bal) - 1 - lane0) : T;
+                    B += xs;
+                    if (xs > 0) moved = true;
+                    if (xs < T) go = false;
+                }
+            }
+        }
+        if (!moved) run = false;
+    }
+    return make_int2(A, B);
+}
+
+// The team moves R's kept entries r0+B .. r0+cR-1 to l0+A+1 onward.  The
+// destination lies below the source, so copying forward T entries at a time,
+// each step's reads before its writes, never overwrites an unread entry.
+// Every lane of the wave calls it.
+__device__ __forceinline__ void team_move(const Arr& ar, int l0, int A, int r0, int B, int cR, int x,
+                                          int T, bool act) {
+    const int n = act ? cR - B : 0;
+    const int dst = l0 + A + 1, src = r0 + B;
+    for (int i0 = 0;; i0 += T) {
+        const int i = i0 + x;
+        const bool a = i < n;
+        if (__ballot(a) == 0) break;
+        double s = 0.0, w = 0.0;
+        int t = 0;
+        if (a) {
+            s = ar.S[src + i];
+            w = ar.W[src + i];
+            t = ar.tag[src + i];
+        }
+        wave_sync();
+        if (a) {
+            ar.S[dst + i] = s;
+            ar.W[dst + i] = w;
+            ar.tag[dst + i] = t;
+        }
+        wave_sync();
+    }
+}
+
+// The bridge of two neighbouring compact hulls by one wave.  The walk of
+// Lemma 4.2 stops at the one pair (A, B) whose line has A's neighbours in L
+// and B's neighbours in R on or above it, A's left neighbour and B's right one
+// strictly above (the outermost of collinear vertices).  These four local
+// conditions single that pair out, so the wave tests the 16 x 16 pairs
+// nearest the shared point at once, four per lane, and walks only when the
+// test does not find exactly one pair.  Every lane of the wave calls it.
+__device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r0, int cR, int lane) {
+    {
+        const Pt PA = ar.pt(l0 + cL - 2), Ps = ar.pt(r0), PB = ar.pt(r0 + 1);
+        if (cross3(PA, Ps, PB) > 0.0) return make_int2(cL - 1, 1);  // convex at the shared point
+    }
+    const int i = lane & 15, b0 = 1 + 4 * (lane >> 4);
+    const int a = cL - 2 - i;
+    unsigned msk = 0;
+    if (a >= 0 && b0 <= cR - 1) {
+        const Pt La = ar.pt(l0 + a), Ln = ar.pt(l0 + a + 1);
+        const Pt Lp = a > 0 ? ar.pt(l0 + a - 1) : La;
+        Pt Rr[6];  // R[b0-1 .. b0+4], clamped to R's last entry
+#pragma unroll
+        for (int k = 0; k < 6; ++k) Rr[k] = ar.pt(r0 + min(b0 - 1 + k, cR - 1));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = b0 + q;
+            if (b <= cR - 1) {
+                const bool c1 = a == 0 || cross3(Lp, La, Rr[q + 1]) > 0.0;
+                const bool c2 = b == cR - 1 || cross3(La, Rr[q + 1], Rr[q + 2]) > 0.0;
+                const bool c3 = cross3(La, Ln, Rr[q + 1]) <= 0.0;
+                const bool c4 = cross3(La, Rr[q], Rr[q + 1]) <= 0.0;
+                if (c1 && c2 && c3 && c4) msk |= 1u << q;
+            }
+        }
+    }
+    const uint64_t bal = __ballot(msk != 0);
+    if (__popcll(bal) == 1) {
+        const int f = __ffsll((long long)bal) - 1;
+        const unsigned fm = (unsigned)__shfl((int)msk, f);
+        if (__popc(fm) == 1) return make_int2(cL - 2 - (f & 15), 1 + 4 * (f >> 4) + (__ffs((int)fm) - 1));
+    }
+    return team_bridge(ar, l0, cL, r0, cR, lane, 64, 0, true);
+}
+
+// Merges the nodes of a compact-array tree level by level: node k of the
+// first level is entries k*E .. k*E+cnt[k]-1; at each level node a and node
+// a+span merge into node a, one wave per merge.  Leaves the root's hull in
+// entries 0..cnt[0]-1.
+template <int NT>
+__device__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn, int E) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    for (int span = 1; span < nn; span <<= 1) {
+        const int nm = (nn - span + 2 * span - 1) / (2 * span);
+        for (int k = wid; k < nm; k += NW) {
+            const int a = 2 * k * span, b = a + span;
+            const int cL = cnt[a], cR = cnt[b];
+            const int2 br = wave_bridge(ar, a * E, cL, b * E, cR, lane);
+            team_move(ar, a * E, br.x, b * E, br.y, cR, lane, 64, true);
+            if (lane == 0) cnt[a] = br.x + 1 + cR - br.y;
+        }
+        __syncthreads();
+    }
+}
+
+// Reconstruction records (Corollary 4.5) from a root list of nroot segments
+// D (LDS or workspace), at most one per chunk and in chunk order.  Per chunk
+// j, the index of the first segment whose chunk is >= j is the number of
+// segments in earlier chunks: a scan over the chunks (in fs, m ints)
+// instead of a search per chunk.
+template <int NT>
+__device__ void write_records_scan(const RowView X, const uint2* D, int nroot, int m, int32_t* vb,
+                                   int32_t* fs, ChunkRec* rec, int* ired) {
+    const int tid = threadIdx.x;
+    for (int j = tid; j < m; j += NT) fs[j] = 0;
+    __syncthreads();
+    for (int i = tid; i < nroot; i += NT) fs[dchunk(D[i])] = 1;
+    __syncthreads();
+    int carry = 0, vcarry = 0;
+    const int top = max(m, nroot);
+    for (int t0 = 0; t0 < top; t0 += NT) {
+        const int j = t0 + tid;
+        int tot;
+        const int f = j < m ? fs[j] : 0;
+        const int xj = wg_excl_scan_int<NT>(f, ired, &tot);
+        if (j < m) fs[j] = carry + xj;
+        carry += tot;
+        int v = 0;
+        if (j < nroot) {
+            const uint2 d = D[j];
+            v = dhi(d) - dlo(d) + 1;
+        }
+        const int xv = wg_excl_scan_int<NT>(v, ired, &tot);
+        if (j < nroot) vb[j] = vcarry + xv;
+        vcarry += tot;
+    }
+    __syncthreads();
+    for (int j = tid; j < m; j += NT) {
+        const int i = fs[j];  // first root segment with chunk >= j
+        const uint2 d = D[min(i, nroot - 1)];
+        ChunkRec rc;
+        rc.pad = 0;
+        if (i < nroot && dchunk(d) == j) {
+            rc.vb = vb[i];
+            rc.lo = dlo(d);
+            rc.hi = dhi(d);
+            rc.slope_in = 0.0;
+            rc.slope_out = 0.0;
+            if (i > 0) {
+                const uint2 p = D[i - 1];
+                const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
+                rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+            }
+            if (i + 1 < nroot) {
+                const uint2 q = D[i + 1];
+                const Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
+                rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
+            }
+        } else {
+            // the chunk lies under one edge, from the last vertex of the
+            // previous segment to the first vertex of the next (chunk 0
+            // always holds the row's first point, so i >= 1)
+            const uint2 p = D[i - 1];
+            const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
+            rc.vb = vb[i];
             rc.lo = -1;
             rc.hi = -1;
             rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);

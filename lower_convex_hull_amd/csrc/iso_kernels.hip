@@ -30,60 +30,75 @@ namespace iso {
 namespace {
 
 // ----------------------------------------------------------------------------
-// The hull of one workgroup's points.
+// The hull of one workgroup's points, kept as compact vertex arrays in LDS.
 //
-// Thread L owns points L*P .. L*P+P of the block (P+1 points; its last point
-// is thread L+1's first).  Bits 0..P-1 of mask[L] mark which of points
-// L*P .. L*P+P-1 are vertices; the block's last point NT*P is always one.
+// Thread L owns points L*P .. L*P+P (P+1 points; its last point is thread
+// L+1's first) and a region of RS = P+1 array entries starting at L*RS.  Its
+// thread hull, a monotone chain over its locally convex points (paper section
+// 3.1), is built with the region as the stack.  Neighbouring hulls are then
+// merged pairwise, level by level (section 3.2): one thread walks the two arrays
+// to the bridge (Lemma 4.2), testing four candidates per LDS round trip since
+// their positions are known, and the group's threads move the right array's
+// kept vertices down behind the left array's kept ones.  A node of level r
+// thus holds its hull at the start of its first thread's region, and the
+// workgroup's hull ends up at the start of region 0.
 // ----------------------------------------------------------------------------
 template <int NT, int P, bool WT>
 struct HullSmem {
-    // block-relative S_k and W_k, stored at sk(k) = k + k / P: each thread's
-    // points plus one pad slot, so that threads reading their own points (and
-    // walkers reading points P apart) hit different LDS banks
-    double S[NT * (P + 1) + 1];
-    double W[WT ? NT * (P + 1) + 1 : 1];
-    int16_t prv[NT * P + 1];        // hull neighbours of each vertex (the walks' links)
-    int16_t nxt[NT * P + 1];
-    uint32_t mask[NT];
-    int16_t bra[2 * NT];            // bridge ends of every merge, by round
-    int16_t brb[2 * NT];
+    static constexpr int RS = P + 1;
+    double S[NT * RS];           // block-relative S of each array entry
+    double W[WT ? NT * RS : 1];  // block-relative W (weighted; else W is the index)
+    uint16_t idx[NT * RS];       // block point index of each entry
+    int32_t cnt[NT];             // entries of the node stored from this region
+    int32_t mvk[NT];             // per merge: kept entries of the left array
+    int32_t mvb[NT];             // per merge: first kept entry of the right array
     double red[NT / 64 + 1];
     int ired[NT / 64 + 1];
+    double end_s, end_w;         // S and W of point len (padding points repeat it)
     int flag;
 };
 
-template <int P>
-__device__ __forceinline__ int sk(int k) {
-    return k + k / P;
+// Exclusive and inclusive workgroup scans of one f64 value per thread.  The
+// wave totals are added in wave order, so thread L's inclusive value is
+// bit-identical to thread L+1's exclusive value.
+template <int NT>
+__device__ __forceinline__ void wg_scan2(double v, double* red, double& excl, double& incl) {
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    double x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double t = __shfl_up(x, d);
+        if (lane >= d) x += t;
+    }
+    double ex = __shfl_up(x, 1);
+    if (lane == 0) ex = 0.0;
+    if (lane == 63) red[wid] = x;
+    __syncthreads();
+    double before = 0.0;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k)
+        if (k < wid) before += red[k];
+    excl = before + ex;
+    incl = before + x;
 }
 
-template <int NT, int P, bool WT>
-struct Block {
-    HullSmem<NT, P, WT>& sm;
-    int len;  // real elements in the block; points beyond len repeat point len
-
-    __device__ __forceinline__ Pt pt(int k) const {
-        Pt p;
-        p.s = sm.S[sk<P>(k)];
-        p.w = WT ? sm.W[sk<P>(k)] : (double)min(k, len);
-        return p;
-    }
+// Result of block_hull: either every point 0..len is a vertex (`all`), or the
+// hull's h vertices are entries 0..h-1 of the LDS arrays.
+struct HullOut {
+    bool all;
+    int h;
 };
 
-// Makes one lane's LDS writes visible to the other lanes of its wave and keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Loads the block's elements, forms the block-relative cumulative sums, and
-// leaves in sm.mask the vertices of the block's lower hull.  Returns this
-// thread's element values (sign applied, sanitised) in yv.
+// builds the block's lower hull.  Returns this thread's element values (sign
+// applied, sanitised) in yv and its points' S (and W) in ps/pw: ps[b] is point
+// base+b+1.
 template <int NT, int P, bool WT>
-__device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
-                           const float* __restrict__ gw, int len, float sign, float (&yv)[P]) {
+__device__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
+                              const float* __restrict__ gw, int len, float sign, float (&yv)[P],
+                              double (&ps)[P], double (&pw)[P], double& s0, double& w0) {
+    constexpr int RS = P + 1;
     const int L = threadIdx.x;
     const int base = L * P;
     float wv[P];
@@ -111,6 +126,10 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
             if (WT) wr[b] = e < len ? gw[e] : 0.0f;
         }
     }
+    // the element before this thread's first (for the increasing test)
+    float yp = (L > 0 && base <= len) ? gy[base - 1] : 0.0f;
+    if (!isfinite(yp)) yp = 0.0f;
+    yp *= sign;
 #pragma unroll
     for (int b = 0; b < P; ++b) {
         int e = base + b;
@@ -129,8 +148,6 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
     }
 
     // ---- prefix sums (paper section 2.1, equation (2)), in f64
-    double ps[P];
-    double pw[P];
     double ls = 0.0, lw = 0.0;
 #pragma unroll
     for (int b = 0; b < P; ++b) {
@@ -143,162 +160,205 @@ __device__ void block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy
         }
         ps[b] = ls;
     }
-    double tot;
-    double xs = wg_excl_scan<NT>(ls, sm.red, &tot);
-    double xw = 0.0;
-    if (WT) xw = wg_excl_scan<NT>(lw, sm.red, &tot);
+    double xs, xs1, xw = 0.0, xw1 = 0.0;
+    wg_scan2<NT>(ls, sm.red, xs, xs1);
+    __syncthreads();
+    if (WT) {
+        wg_scan2<NT>(lw, sm.red, xw, xw1);
+        __syncthreads();
+    }
+    // point base+b+1 for b < P-1 is xs + ps[b]; the thread's last point is the
+    // next thread's first
+#pragma unroll
+    for (int b = 0; b < P - 1; ++b) {
+        ps[b] = xs + ps[b];
+        if (WT) pw[b] = xw + pw[b];
+    }
+    ps[P - 1] = xs1;
+    if (WT) pw[P - 1] = xw1;
+    s0 = xs;
+    w0 = WT ? xw : (double)min(base, len);
+    // point len: padding points (beyond len) become exact copies of it
 #pragma unroll
     for (int b = 0; b < P; ++b) {
-        sm.S[sk<P>(base + b + 1)] = xs + ps[b];
-        if (WT) sm.W[sk<P>(base + b + 1)] = xw + pw[b];
-    }
-    if (L == 0) {
-        sm.S[0] = 0.0;
-        if (WT) sm.W[0] = 0.0;
+        if (base + b + 1 == len) {
+            sm.end_s = ps[b];
+            sm.end_w = WT ? pw[b] : (double)len;
+        }
     }
     if (bad) atomicOr(&sm.flag, bad);
 
-    // ---- candidates: point k is a vertex only if the slope into it (the
-    // value of element k-1) is below the slope out of it (element k).  Points
-    // next to a padding element are kept as candidates; padding points
-    // (beyond len) that are not thread ends are dropped, since they repeat
-    // point len.
+    // ---- is the row strictly increasing here?  Then every point is a vertex
+    // (each edge's slope is its element; paper section 2.1).
+    bool inc = L == 0 || base >= len || yp < yv[0];
+#pragma unroll
+    for (int b = 1; b < P; ++b)
+        if (base + b < len) inc = inc && yv[b - 1] < yv[b];
+    const bool all = __syncthreads_and(inc) != 0;  // also publishes end_s, end_w
+    if (base + P > len) {
+        const double es = sm.end_s, ew = sm.end_w;
+        if (base >= len) { s0 = es; w0 = ew; }
+#pragma unroll
+        for (int b = 0; b < P; ++b)
+            if (base + b + 1 > len) { ps[b] = es; if (WT) pw[b] = ew; }
+    }
+    if (all) return HullOut{true, len + 1};
+
+    // ---- candidates: point k is a vertex only if the slope into it (element
+    // k-1) is below the slope out of it (element k).  Points next to a padding
+    // element are kept; padding points that are not thread ends are dropped.
     uint32_t cand = 1u | (1u << P);
 #pragma unroll
     for (int k = 1; k < P; ++k) {
-        int pidx = base + k;
-        bool realL = pidx - 1 < len, realR = pidx < len;
+        const int pidx = base + k;
         bool c;
         if (pidx > len) c = false;
-        else if (realL && realR) c = yv[k - 1] < yv[k];
+        else if (pidx < len) c = yv[k - 1] < yv[k];
         else c = true;
         if (c) cand |= 1u << k;
     }
-    __syncthreads();
 
-    Block<NT, P, WT> B{sm, len};
+    auto ent = [&](int i) -> Pt {
+        Pt p;
+        p.s = sm.S[i];
+        p.w = WT ? sm.W[i] : (double)min((int)sm.idx[i], len);
+        return p;
+    };
 
-    // ---- thread hull: monotone chain over the candidates, the stack a bit
-    // mask (paper section 3.1).  Each pass pops or pushes; both outcomes need
-    // one LDS load, whose address is selected first.
-    const uint32_t full = (P == 31) ? 0xffffffffu : ((2u << P) - 1u);
-    uint32_t stk;
-    if (cand == full) {
-        stk = full;  // every point locally convex: the chain keeps them all
-    } else {
-        stk = 1u;
-        int t = 0, u = -1;
-        Pt T = B.pt(base), U = T;
-        uint32_t rest = cand & ~1u;
-        int c = lsb32(rest);
-        Pt Cp = B.pt(base + c);
-        for (int it = 0; it < 2 * P + 2 && c <= P; ++it) {
-            bool pop = (u >= 0) && (cross3(U, T, Cp) <= 0.0);
-            int addr;
-            if (pop) {
-                stk &= ~(1u << t);
-                t = u;
-                T = U;
-                uint32_t below = stk & ((1u << u) - 1u);
-                u = below ? msb32(below) : -1;
-                addr = u < 0 ? 0 : u;
-            } else {
-                stk |= 1u << c;
-                u = t;
-                U = T;
-                t = c;
-                T = Cp;
-                uint32_t above = cand & ~((2u << c) - 1u);
-                c = above ? lsb32(above) : P + 1;
-                addr = c > P ? P : c;
-            }
-            Pt Lp = B.pt(base + addr);
-            if (pop) U = Lp;
-            else Cp = Lp;
-        }
-    }
-    uint32_t my = stk & ((1u << P) - 1u);
-    sm.mask[L] = my;
-    __syncthreads();
-
-    // ---- links between consecutive vertices of the thread hulls; a thread's
-    // last point is the next thread's first (bit 0, always a vertex)
+    // ---- thread hull: monotone chain, the region as its stack; pushes come
+    // from registers, a pop reloads the entry under the new top
+    const int r0 = L * RS;
     {
-        const uint32_t pm = L > 0 ? sm.mask[L - 1] : 0u;
-        int prev_v = L > 0 ? (L - 1) * P + msb32(pm) : 0;
-        uint32_t bits = my;
-        while (bits) {
-            const int b = lsb32(bits);
-            bits &= bits - 1u;
-            const int k = base + b;
-            sm.prv[k] = (int16_t)prev_v;
-            sm.nxt[k] = (int16_t)(bits ? base + lsb32(bits) : base + P);
-            prev_v = k;
+        Pt T{w0, s0}, U{0.0, 0.0};
+        sm.S[r0] = s0;
+        if (WT) sm.W[r0] = w0;
+        sm.idx[r0] = (uint16_t)base;
+        int dep = 1;
+#pragma unroll
+        for (int b = 1; b <= P; ++b) {
+            if (!((cand >> b) & 1u)) continue;
+            const Pt Cp{WT ? pw[b - 1] : (double)min(base + b, len), ps[b - 1]};
+            while (dep >= 2 && cross3(U, T, Cp) <= 0.0) {
+                --dep;
+                T = U;
+                if (dep >= 2) U = ent(r0 + dep - 2);
+            }
+            sm.S[r0 + dep] = Cp.s;
+            if (WT) sm.W[r0 + dep] = Cp.w;
+            sm.idx[r0 + dep] = (uint16_t)(base + b);
+            ++dep;
+            U = T;
+            T = Cp;
         }
-        if (L == NT - 1) sm.prv[NT * P] = (int16_t)prev_v;
+        sm.cnt[L] = dep;
     }
     __syncthreads();
 
-    // ---- merge the thread hulls pairwise (paper section 3.2; Lemma 4.2's
-    // walk).  The first thread of each pair of groups walks to the bridge over
-    // the links and relinks its two ends; the rounds inside a wave need no
-    // workgroup barrier.  The removed vertices' bits are cleared at the end.
+    // ---- merge the hulls pairwise
     constexpr int R = __builtin_ctz(NT);
     for (int r = 0; r < R; ++r) {
         const int g = 2 << r, half = 1 << r;
+        if (g > 64) __syncthreads();  // the two halves were built by different waves
         if ((L & (g - 1)) == 0) {
-            const int lo_pt = L * P, hi_pt = (L + g) * P;
-            const int s = (L + half) * P;
-            int a = sm.prv[s];
-            int b = sm.nxt[s];
-            Pt Pa = B.pt(a), Ps = B.pt(s), Pb = B.pt(b);
-            if (cross3(Pa, Ps, Pb) > 0.0) {
-                a = s;
-                b = s;  // convex at s: nothing removed
+            const int a0 = L * RS, b0 = (L + half) * RS;
+            const int cL = sm.cnt[L], cR = sm.cnt[L + half];
+            int A = cL - 2, B = 1;
+            Pt PA = ent(a0 + A), PB = ent(b0 + 1);
+            const Pt Ps = ent(b0);
+            if (cross3(PA, Ps, PB) > 0.0) {
+                A = cL - 1;  // convex at the shared point: kept once, in L
             } else {
-                // a moves left while its turn towards b is not strictly left,
-                // b moves right likewise, until neither moves.  Every move
-                // removes a vertex, so the walk ends; the cap only guards.
-                for (int pass = 0; pass < 2 * NT * P + 4; ++pass) {
+                // A moves left while its turn towards B is not strictly left,
+                // B moves right likewise, until neither moves
+                for (int pass = 0; pass < 2 * NT * RS; ++pass) {
                     bool moved = false;
-                    while (a > lo_pt) {
-                        const int a2 = sm.prv[a];
-                        const Pt P2 = B.pt(a2);
-                        if (cross3(P2, Pa, Pb) <= 0.0) { a = a2; Pa = P2; moved = true; }
-                        else break;
+                    while (A > 0) {
+                        const Pt c1 = ent(a0 + A - 1), c2 = ent(a0 + max(A - 2, 0));
+                        const Pt c3 = ent(a0 + max(A - 3, 0)), c4 = ent(a0 + max(A - 4, 0));
+                        if (cross3(c1, PA, PB) > 0.0) break;
+                        --A; PA = c1; moved = true;
+                        if (A == 0 || cross3(c2, PA, PB) > 0.0) break;
+                        --A; PA = c2;
+                        if (A == 0 || cross3(c3, PA, PB) > 0.0) break;
+                        --A; PA = c3;
+                        if (A == 0 || cross3(c4, PA, PB) > 0.0) break;
+                        --A; PA = c4;
                     }
-                    while (b < hi_pt) {
-                        const int b2 = sm.nxt[b];
-                        const Pt P2 = B.pt(b2);
-                        if (cross3(Pa, Pb, P2) <= 0.0) { b = b2; Pb = P2; moved = true; }
-                        else break;
+                    while (B < cR - 1) {
+                        const Pt c1 = ent(b0 + B + 1), c2 = ent(b0 + min(B + 2, cR - 1));
+                        const Pt c3 = ent(b0 + min(B + 3, cR - 1)), c4 = ent(b0 + min(B + 4, cR - 1));
+                        if (cross3(PA, PB, c1) > 0.0) break;
+                        ++B; PB = c1; moved = true;
+                        if (B == cR - 1 || cross3(PA, PB, c2) > 0.0) break;
+                        ++B; PB = c2;
+                        if (B == cR - 1 || cross3(PA, PB, c3) > 0.0) break;
+                        ++B; PB = c3;
+                        if (B == cR - 1 || cross3(PA, PB, c4) > 0.0) break;
+                        ++B; PB = c4;
                     }
                     if (!moved) break;
                 }
-                sm.nxt[a] = (int16_t)b;
-                sm.prv[b] = (int16_t)a;
             }
-            sm.bra[(NT >> r) + (L >> (r + 1))] = (int16_t)a;
-            sm.brb[(NT >> r) + (L >> (r + 1))] = (int16_t)b;
+            sm.mvk[L] = A + 1;
+            sm.mvb[L] = B;
+            sm.cnt[L] = A + 1 + cR - B;
         }
-        if (g < 64) wave_sync();
+        if (g <= 64) wave_sync();
         else __syncthreads();
-    }
-    if (NT <= 64) __syncthreads();
-    // ---- clear the bits of vertices strictly inside any bridge of this
-    // thread's groups
-    for (int r = 0; r < R; ++r) {
-        const int i = (NT >> r) + (L >> (r + 1));
-        const int a = sm.bra[i], b = sm.brb[i];
-        const int k0 = max(a + 1, base), k1 = min(b - 1, base + P - 1);
-        if (k0 <= k1) {
-            const uint32_t clr = ((k1 - base == 31) ? 0xffffffffu : ((2u << (k1 - base)) - 1u)) &
-                                 ~((1u << (k0 - base)) - 1u);
-            my &= ~clr;
+        // move the right array's kept entries down behind the left's (the
+        // destination always lies below the source, so a forward copy in
+        // steps of the group size never overwrites an entry it has yet to read)
+        const int Lg = L & ~(g - 1), x = L & (g - 1);
+        const int kept = sm.mvk[Lg];
+        const int dst = Lg * RS + kept, src = (Lg + half) * RS + sm.mvb[Lg];
+        const int n = sm.cnt[Lg] - kept;
+        if (g <= 64) {
+            for (int i0 = 0;; i0 += g) {
+                const int i = i0 + x;
+                const bool act = i < n;
+                if (__ballot(act) == 0) break;
+                double cs = 0.0, cw = 0.0;
+                uint16_t ci = 0;
+                if (act) {
+                    cs = sm.S[src + i];
+                    if (WT) cw = sm.W[src + i];
+                    ci = sm.idx[src + i];
+                }
+                wave_sync();
+                if (act) {
+                    sm.S[dst + i] = cs;
+                    if (WT) sm.W[dst + i] = cw;
+                    sm.idx[dst + i] = ci;
+                }
+                wave_sync();
+            }
+        } else {
+            // groups span waves: the same forward copy, a barrier between
+            // each step's reads and writes (trip count uniform over the block)
+            int nmax = 0;
+            for (int q = 0; q < NT; q += g) nmax = max(nmax, sm.cnt[q] - sm.mvk[q]);
+            for (int i0 = 0; i0 < nmax; i0 += g) {
+                const int i = i0 + x;
+                const bool act = i < n;
+                double cs = 0.0, cw = 0.0;
+                uint16_t ci = 0;
+                if (act) {
+                    cs = sm.S[src + i];
+                    if (WT) cw = sm.W[src + i];
+                    ci = sm.idx[src + i];
+                }
+                __syncthreads();
+                if (act) {
+                    sm.S[dst + i] = cs;
+                    if (WT) sm.W[dst + i] = cw;
+                    sm.idx[dst + i] = ci;
+                }
+            }
+            __syncthreads();
         }
     }
-    sm.mask[L] = my;
     __syncthreads();
+    return HullOut{false, sm.cnt[0]};
 }
 
 // ----------------------------------------------------------------------------
@@ -316,11 +376,11 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
     const float* gw = WT ? w + row * n : nullptr;
     const int len = (int)n;
     float yv[P];
-    block_hull<NT, P, WT>(sm, gy, gw, len, sign, yv);
+    double ps[P], pw[P], s0, w0;
+    const HullOut ho = block_hull<NT, P, WT>(sm, gy, gw, len, sign, yv, ps, pw, s0, w0);
 
     const int L = threadIdx.x;
     const int base = L * P;
-    const uint32_t my = sm.mask[L];
     const int flag = sm.flag;
     if (L == 0) row_flag[row] = flag;
     float* go = out + row * n;
@@ -335,46 +395,48 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
         }
         return;
     }
-    // vertex before this thread's points (max-scan from the left) and the first
-    // vertex after them (min-scan from the right); vertex count before them.
-    int lastv = my ? base + msb32(my) : -1;
-    int firstv = my ? base + lsb32(my) : NT * P;
-    int cnt = __popc(my);
-    __shared__ int s_last[NT];
-    __shared__ int s_first[NT];
-    s_last[L] = lastv;
-    s_first[L] = firstv;
-    int total;
-    int before = wg_excl_scan_int<NT>(cnt, sm.ired, &total);  // contains a barrier
-    int prev_in = -1;
-    int next_in = NT * P;
-    for (int k = L - 1; k >= 0; --k) {
-        int v = s_last[k];
-        if (v >= 0) { prev_in = v; break; }
+    if (ho.all) {
+        // every point a vertex: each element is its own block
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            const int e = base + b;
+            if (e < len) {
+                go[e] = sign * yv[b];
+                if (gb) gb[e] = e;
+            }
+        }
+        return;
     }
-    for (int k = L + 1; k < NT; ++k) {
-        int v = s_first[k];
-        if (v < NT * P) { next_in = v; break; }
+    // q = the last hull vertex at or before this thread's first element
+    const int h = ho.h;
+    int lo = 0, hi = h;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)sm.idx[mid] <= base) lo = mid + 1;
+        else hi = mid;
     }
-    Block<NT, P, WT> B{sm, len};
+    int q = lo - 1;
+    int qs = -1;
+    float slope = 0.0f;
 #pragma unroll
     for (int b = 0; b < P; ++b) {
-        int e = base + b;
+        const int e = base + b;
         if (e >= len) break;
-        uint32_t upto = (b == 31) ? 0xffffffffu : ((2u << b) - 1u);
-        uint32_t below = my & upto;
-        uint32_t above = my & ~upto;
-        int pv = below ? base + msb32(below) : prev_in;
-        int nv = above ? base + lsb32(above) : next_in;
+        while ((int)sm.idx[q + 1] <= e) ++q;  // vertex q <= e < vertex q+1
+        const int ka = sm.idx[q], kb = sm.idx[q + 1];
         float val;
-        if (pv == e && nv == e + 1) {
+        if (ka == e && kb == e + 1) {
             val = yv[b];  // both ends are vertices: the edge is the element itself
         } else {
-            Pt A = B.pt(pv), C = B.pt(nv);
-            val = (float)((C.s - A.s) / (C.w - A.w));
+            if (qs != q) {
+                const double dw = WT ? sm.W[q + 1] - sm.W[q] : (double)(min(kb, len) - ka);
+                slope = (float)((sm.S[q + 1] - sm.S[q]) / dw);
+                qs = q;
+            }
+            val = slope;
         }
         go[e] = sign * val;
-        if (gb) gb[e] = before + __popc(below) - 1;  // point 0 is always a vertex
+        if (gb) gb[e] = q;
     }
 }
 
@@ -394,43 +456,58 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
     const int64_t off = row * n + (int64_t)j * C;
     const int len = (int)min((int64_t)C, n - (int64_t)j * C);
     float yv[P];
-    block_hull<NT, P, WT>(sm, y + off, WT ? w + off : nullptr, len, sign, yv);
-
+    double ps[P], pw[P], s0, w0;
+    const HullOut ho = block_hull<NT, P, WT>(sm, y + off, WT ? w + off : nullptr, len, sign, yv, ps,
+                                             pw, s0, w0);
     const int L = threadIdx.x;
     const int base = L * P;
-    const uint32_t my = sm.mask[L];
-    int total;
-    int rank = wg_excl_scan_int<NT>(__popc(my), sm.ired, &total);
+    const int h = ho.h;
     const size_t slot = (size_t)gid * (C + 1);
-    const int h = total + 1;
     WinRec* wr = ws.win + gid;
     // window entry of hull rank r, or -1 if r is in the middle of a long hull
     auto wslot = [&](int r) {
         if (h <= 2 * kWinK || r < kWinK) return r;
         return r >= h - kWinK ? kWinK + r - (h - kWinK) : -1;
     };
-    uint32_t bits = my;
-    while (bits) {
-        int b = lsb32(bits);
-        bits &= bits - 1u;
-        int k = base + b;
-        ws.slot_idx[slot + rank] = (uint16_t)min(k, len);
-        ws.slot_S[slot + rank] = sm.S[sk<P>(k)];
-        if (WT) ws.slot_W[slot + rank] = sm.W[sk<P>(k)];
-        const int e = wslot(rank);
-        if (e >= 0) wr->v[e] = make_double2(sm.S[sk<P>(k)], WT ? sm.W[sk<P>(k)] : (double)min(k, len));
-        ++rank;
+    if (ho.all) {
+        // every point 0..len is a vertex: stage the points' S (and W) in LDS
+        // (point k at k + (k-1)/P, so that threads writing their own points hit
+        // different banks), then write the slot with consecutive threads on
+        // consecutive vertices
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            const int k = base + b + 1;
+            sm.S[k + (k - 1) / P] = ps[b];
+            if (WT) sm.W[k + (k - 1) / P] = pw[b];
+        }
+        __syncthreads();
+        for (int i = L; i <= len; i += NT) {
+            const double s = i == 0 ? 0.0 : sm.S[i + (i - 1) / P];
+            const double wv = WT ? (i == 0 ? 0.0 : sm.W[i + (i - 1) / P]) : (double)i;
+            ws.slot_idx[slot + i] = (uint16_t)i;
+            ws.slot_S[slot + i] = s;
+            if (WT) ws.slot_W[slot + i] = wv;
+            const int e = wslot(i);
+            if (e >= 0) wr->v[e] = make_double2(s, wv);
+        }
+    } else {
+        for (int i = L; i < h; i += NT) {
+            const int k = min((int)sm.idx[i], len);
+            const double s = sm.S[i];
+            const double wv = WT ? sm.W[i] : (double)k;
+            ws.slot_idx[slot + i] = (uint16_t)k;
+            ws.slot_S[slot + i] = s;
+            if (WT) ws.slot_W[slot + i] = wv;
+            const int e = wslot(i);
+            if (e >= 0) wr->v[e] = make_double2(s, wv);
+        }
     }
-    if (L == NT - 1) {
-        // the chunk's last point (point len; padding repeats it) ends the hull
-        ws.slot_idx[slot + total] = (uint16_t)len;
-        ws.slot_S[slot + total] = sm.S[sk<P>(C)];
-        if (WT) ws.slot_W[slot + total] = sm.W[sk<P>(C)];
-        wr->v[wslot(total)] = make_double2(sm.S[sk<P>(C)], WT ? sm.W[sk<P>(C)] : (double)len);
+    if (L == 0) {
         wr->h = h;
         ws.hull_cnt[gid] = h;
-        ws.tot_S[gid] = sm.S[sk<P>(C)];
-        if (WT) ws.tot_W[gid] = sm.W[sk<P>(C)];
+        ws.tot_S[gid] = sm.end_s;
+        if (WT) ws.tot_W[gid] = sm.end_w;
         ws.chunk_flag[gid] = sm.flag;
     }
 }

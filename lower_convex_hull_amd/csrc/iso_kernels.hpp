@@ -17,11 +17,13 @@ constexpr int kChunk = kLongNT * kLongP;  // 4096
 constexpr int kShortMax = 4096;
 constexpr int kMergeNT = 1024;
 constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
-constexpr int kWinK = 8;            // hull vertices kept at each end of a chunk's window
+constexpr int kWinK = 16;           // hull vertices kept at each end of a chunk's window
+constexpr int kGWinK = 32;          // the same for a group hull's window
 constexpr int kGroup = 64;          // chunks per group of the first merge stage
-constexpr int kGroupNT = 256;
+constexpr int kGroupNT = 1024;
 constexpr int kTopNT = 1024;
-constexpr int kTopMax = 256;        // groups per row the second stage keeps in LDS
+constexpr int kTopMax = 96;         // groups per row the second stage keeps in LDS
+constexpr int kTopFastMax = 96;     // groups per row for the second stage's compact-array path
 constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed to a wave
 constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
 constexpr int kHardCap = 256;     // merges per level a wave may take over
@@ -57,14 +59,20 @@ struct WinRec {
 };
 
 // The same for the hull of a group of kGroup chunks (first merge stage): its
-// vertex count, the number of segments in its list, and the (S, W) of its
-// first and last kWinK vertices relative to the group's first point.
+// vertex count, the number of segments in its list, the (S, W) of its first
+// and last kGWinK vertices relative to the group's first point, and for each
+// of those the chunk and the position in that chunk's hull (packed by mktag).
 struct GroupWin {
     int32_t h;
     int32_t nseg;
     int32_t pad[2];
-    double2 v[2 * kWinK];
+    double2 v[2 * kGWinK];
+    int32_t tag[2 * kGWinK];
 };
+
+// A vertex's chunk and its position in that chunk's hull, in one int32.
+constexpr int kTagShift = 13;  // positions 0..kChunk need 13 bits
+constexpr int kTagMaxChunks = 1 << (31 - kTagShift);
 
 // Device pointers of the long-row workspace (see plan_long in iso_api.hip).
 struct LongWs {

@@ -275,7 +275,7 @@ struct GroupView {
     __device__ __forceinline__ Pt vtx(int g, int pos, int gr) const {
         const int h = gh[g];
         int e = pos;
-        if (h > 2 * kWinK && pos >= kWinK) e = pos >= h - kWinK ? kWinK + pos - (h - kWinK) : -1;
+        if (h > 2 * kGWinK && pos >= kGWinK) e = pos >= h - kGWinK ? kGWinK + pos - (h - kGWinK) : -1;
         double s, w;
         if (e >= 0) {
             const double2 v = gw[g].v[e];
@@ -306,8 +306,12 @@ struct GroupView {
 
 template <bool WT>
 __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
-    constexpr int NT = kGroupNT, G = kGroup;
-    __shared__ WinRec Wn[G];
+    constexpr int NT = kGroupNT, G = kGroup, E = 2 * kWinK, EG = 2 * kGWinK;
+    static_assert(G == 64, "one wave numbers a group's segments");
+    // the generic path's chunk windows, or the fast path's compact arrays
+    constexpr size_t kGen = sizeof(WinRec) * G;
+    constexpr size_t kFast = (size_t)G * E * (8 + 8 + 4);
+    __shared__ __align__(16) unsigned char pool[kGen > kFast ? kGen : kFast];
     __shared__ double lS[G], lW[G];
     __shared__ int32_t HC[G], CNT[G], pre[G + 1];
     __shared__ uint2 D[G], SCR[G];
@@ -315,7 +319,8 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     __shared__ int s_nhard;
     __shared__ int4 s_hard[G / 2];
     __shared__ int ired[NT / 64 + 1];
-    __shared__ int sflag;
+    __shared__ int sflag, s_nseg;
+    __shared__ int sfirst[G], slast[G];
     const int64_t gid = blockIdx.x;
     const int64_t row = gid / ng;
     const int g = (int)(gid - row * ng);
@@ -323,12 +328,13 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     const int j0 = g * G, gc = min(G, m - j0);
     const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
 
-    {
-        const double2* src = reinterpret_cast<const double2*>(ws.win + rb + j0);
-        double2* dst = reinterpret_cast<double2*>(Wn);
-        const int nv2 = gc * (int)(sizeof(WinRec) / sizeof(double2));
-        for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+    // hull counts; the fast path needs every chunk hull whole in its window
+    int hc = 0;
+    if (tid < gc) {
+        hc = ws.hull_cnt[rb + j0 + tid];
+        HC[tid] = hc;
     }
+    const bool fast = __syncthreads_and(tid >= gc || hc <= E) != 0;
     if (wid == 0) {
         // chunk starts relative to the group: a scan of the chunk totals
         double ts = wlane < gc ? ws.tot_S[rb + j0 + wlane] : 0.0;
@@ -351,51 +357,109 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         if (wlane == 0) ws.gtot[row * ng + g] = make_double2(totS, WT ? totW : 0.0);
     }
     __syncthreads();
-    for (int i = tid; i < gc; i += NT) {
-        HC[i] = Wn[i].h;
-        D[i] = mkdesc(i, 0, Wn[i].h - 1);
-        CNT[i] = 1;
-    }
-    __syncthreads();
     const size_t sl = (size_t)(rb + j0) * (kChunk + 1);
-    const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT};
-    for (int span = 1; span < gc; span <<= 1)
-        merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
-
-    // ---- the group's list, its vertex prefix, and its window
-    const int nseg = CNT[0];
-    if (wid == 0) {
-        int v = 0;
-        if (wlane < nseg) v = dhi(D[wlane]) - dlo(D[wlane]) + 1;
-        int x = v;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int u = __shfl_up(x, d);
-            if (wlane >= d) x += u;
+    GroupWin* gwo = ws.gwin + row * ng + g;
+    int nseg, hg;
+    if (fast) {
+        // ---- every chunk hull is short: merge compact arrays in LDS
+        double* aS = reinterpret_cast<double*>(pool);
+        const Arr ar{aS, aS + G * E, reinterpret_cast<int32_t*>(aS + 2 * G * E)};
+        for (int t = tid; t < gc * E; t += NT) {
+            const int i = t / E, e = t - i * E;
+            if (e < HC[i]) {
+                const double2 v = ws.win[rb + j0 + i].v[e];
+                ar.S[t] = lS[i] + v.x;
+                ar.W[t] = lW[i] + v.y;
+                ar.tag[t] = mktag(i, e);
+            }
         }
-        if (wlane < nseg) pre[wlane + 1] = x;
-        if (wlane == 0) pre[0] = 0;
+        for (int i = tid; i < gc; i += NT) {
+            CNT[i] = HC[i];
+            sfirst[i] = -1;
+        }
+        __syncthreads();
+        merge_arrays<NT>(ar, CNT, gc, E);
+        hg = CNT[0];
+        // the group's list: one segment per run of a chunk's vertices
+        for (int t = tid; t < hg; t += NT) {
+            const int c = tchunk(ar.tag[t]);
+            if (t == 0 || tchunk(ar.tag[t - 1]) != c) sfirst[c] = t;
+            if (t == hg - 1 || tchunk(ar.tag[t + 1]) != c) slast[c] = t;
+        }
+        __syncthreads();
+        if (wid == 0) {
+            const bool has = wlane < gc && sfirst[wlane] >= 0;
+            const uint64_t bal = __ballot(has);
+            const int sidx = __popcll(bal & ((1ull << wlane) - 1ull));
+            if (has) {
+                D[sidx] = mkdesc(wlane, tpos(ar.tag[sfirst[wlane]]), tpos(ar.tag[slast[wlane]]));
+                pre[sidx] = sfirst[wlane];
+            }
+            if (wlane == 0) {
+                s_nseg = __popcll(bal);
+                pre[__popcll(bal)] = hg;
+            }
+        }
+        __syncthreads();
+        nseg = s_nseg;
+        const int nwin = min(hg, EG);
+        for (int t = tid; t < nwin; t += NT) {
+            const int r = (hg <= EG || t < kGWinK) ? t : hg - EG + t;
+            gwo->v[t] = make_double2(ar.S[r], ar.W[r]);
+            gwo->tag[t] = mktag(j0 + tchunk(ar.tag[r]), tpos(ar.tag[r]));
+        }
+    } else {
+        // ---- segment lists over the chunk hulls' windows
+        WinRec* Wn = reinterpret_cast<WinRec*>(pool);
+        {
+            const double2* src = reinterpret_cast<const double2*>(ws.win + rb + j0);
+            double2* dst = reinterpret_cast<double2*>(Wn);
+            const int nv2 = gc * (int)(sizeof(WinRec) / sizeof(double2));
+            for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+        }
+        for (int i = tid; i < gc; i += NT) {
+            D[i] = mkdesc(i, 0, HC[i] - 1);
+            CNT[i] = 1;
+        }
+        __syncthreads();
+        const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT};
+        for (int span = 1; span < gc; span <<= 1)
+            merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
+        nseg = CNT[0];
+        if (wid == 0) {
+            int v = 0;
+            if (wlane < nseg) v = dhi(D[wlane]) - dlo(D[wlane]) + 1;
+            int x = v;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                int u = __shfl_up(x, d);
+                if (wlane >= d) x += u;
+            }
+            if (wlane < nseg) pre[wlane + 1] = x;
+            if (wlane == 0) pre[0] = 0;
+        }
+        __syncthreads();
+        hg = pre[nseg];
+        const int nwin = min(hg, EG);
+        for (int t = tid; t < nwin; t += NT) {
+            const int r = (hg <= EG || t < kGWinK) ? t : hg - EG + t;
+            int lo = 0, hi = nseg - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pre[mid] <= r) lo = mid;
+                else hi = mid - 1;
+            }
+            const uint2 d = D[lo];
+            const int pos = dlo(d) + (r - pre[lo]);
+            const Pt v = X.vtx(dchunk(d), pos, 0);
+            gwo->v[t] = make_double2(v.s, v.w);
+            gwo->tag[t] = mktag(j0 + dchunk(d), pos);
+        }
     }
-    __syncthreads();
-    const int hg = pre[nseg];
     for (int i = tid; i < nseg; i += NT) {
         const uint2 d = D[i];
         ws.desc[rb + j0 + i] = mkdesc(j0 + dchunk(d), dlo(d), dhi(d));
         ws.gpre[rb + j0 + i] = pre[i];
-    }
-    GroupWin* gwo = ws.gwin + row * ng + g;
-    const int nwin = min(hg, 2 * kWinK);
-    for (int t = tid; t < nwin; t += NT) {
-        const int r = (hg <= 2 * kWinK || t < kWinK) ? t : hg - 2 * kWinK + t;
-        int lo = 0, hi = nseg - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= r) lo = mid;
-            else hi = mid - 1;
-        }
-        const uint2 d = D[lo];
-        const Pt v = X.vtx(dchunk(d), dlo(d) + (r - pre[lo]), 0);
-        gwo->v[t] = make_double2(v.s, v.w);
     }
     if (tid == 0) {
         gwo->h = hg;
@@ -408,7 +472,9 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         int f = 0;
         for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
         if (f) atomicOr(&sflag, f);
-        write_records<NT>(X, D, nseg, m, ws.vb + rb, ws.rec + rb, ired);
+        const RowView Xr{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
+                         lS, lW, WT};
+        write_records_scan<NT>(Xr, D, nseg, m, ws.vb + rb, sfirst, ws.rec + rb, ired);
         __syncthreads();
         if (tid == 0) ws.row_flag[row] = sflag;
     }
@@ -416,36 +482,32 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
 
 template <bool WT>
 __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
-    constexpr int NT = kTopNT, G = kGroup;
+    constexpr int NT = kTopNT, G = kGroup, E = 2 * kGWinK;
     extern __shared__ int4 top_lds[];
     __shared__ double red[NT / 64 + 1];
     __shared__ int ired[NT / 64 + 1];
     __shared__ int s_nhard;
     __shared__ int4 s_hard[kHardCap];
     __shared__ int sflag;
+    __shared__ int s_ilo[kTopMax], s_ihi[kTopMax], s_off[kTopMax + 1];
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m, gb = row * ng;
     const int tid = threadIdx.x;
-    int4* D = top_lds;
-    int4* SCR = D + ng;
-    GroupWin* GW = reinterpret_cast<GroupWin*>(SCR + ng);
-    double* gS = reinterpret_cast<double*>(GW + ng);
-    double* gW = gS + ng;
-    int2* MI = reinterpret_cast<int2*>(gW + ng);
-    int32_t* CNT = reinterpret_cast<int32_t*>(MI + (ng / 2 + 1));
-    int32_t* GH = CNT + ng;
 
-    {
-        const double2* src = reinterpret_cast<const double2*>(ws.gwin + gb);
-        double2* dst = reinterpret_cast<double2*>(GW);
-        const int nv2 = ng * (int)(sizeof(GroupWin) / sizeof(double2));
-        for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
-    }
+    // group hull counts; the fast path needs every group hull whole in its window
+    int hgv = 0;
+    if (tid < ng) hgv = ws.gwin[gb + tid].h;
+    const bool fast = (__syncthreads_and(tid >= ng || hgv <= E) != 0) && ng <= kTopFastMax &&
+                      m < kTagMaxChunks;
     if (tid == 0) sflag = 0;
     __syncthreads();
     int f = 0;
     for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
     if (f) atomicOr(&sflag, f);
+
+    // group starts (exclusive scan of the group totals)
+    double* gS = reinterpret_cast<double*>(top_lds);
+    double* gW = gS + ng;
     double cS = 0.0, cW = 0.0;
     for (int t0 = 0; t0 < ng; t0 += NT) {
         const int g = t0 + tid;
@@ -462,57 +524,126 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             gW[g] = (double)((int64_t)g * G * kChunk);
         }
     }
-    for (int g = tid; g < ng; g += NT) {
-        GH[g] = GW[g].h;
-        D[g] = make_int4(g, 0, GW[g].h - 1, 0);
-        CNT[g] = 1;
-    }
     __syncthreads();
-    const size_t sl = (size_t)rb * (kChunk + 1);
-    const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
-                     ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
-    const GroupView X{GW, GH, gS, gW, ws.desc + rb, ws.gpre + rb, ws.cst + rb, Cv, WT};
-    for (int span = 1; span < ng; span <<= 1)
-        merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
-
-    // ---- the root list over groups, as segments of chunk hulls
-    const int nr2 = CNT[0];
-    uint2* R = ws.desc_scr + rb;
-    int carry = 0;
-    for (int t0 = 0; t0 < nr2; t0 += NT) {
-        const int t = t0 + tid;
-        int ilo = 0, ihi = 0, g = 0, lo = 0, hi = 0;
-        if (t < nr2) {
-            const int4 d = D[t];
-            g = d.x;
-            lo = d.y;
-            hi = d.z;
-            const int base = g * G, ns = GW[g].nseg;
-            auto seg_of = [&](int p) {
-                int a = 0, b = ns - 1;
-                while (a < b) {
-                    const int mid = (a + b + 1) >> 1;
-                    if (ws.gpre[rb + base + mid] <= p) a = mid;
-                    else b = mid - 1;
-                }
-                return a;
-            };
-            ilo = seg_of(lo);
-            ihi = seg_of(hi);
-        }
-        int tot;
-        const int x = wg_excl_scan_int<NT>(t < nr2 ? ihi - ilo + 1 : 0, ired, &tot);
-        if (t < nr2) {
-            const int base = g * G;
-            for (int i = ilo; i <= ihi; ++i) {
-                const uint2 d = ws.desc[rb + base + i];
-                const int pre_i = ws.gpre[rb + base + i];
-                const int a = i == ilo ? dlo(d) + (lo - pre_i) : dlo(d);
-                const int b = i == ihi ? dlo(d) + (hi - pre_i) : dhi(d);
-                R[carry + x + (i - ilo)] = mkdesc(dchunk(d), a, b);
+    uint2* R = ws.desc_scr + rb;  // the root list, as segments of chunk hulls
+    int nroot;
+    if (fast) {
+        // ---- every group hull is short: merge compact arrays in LDS
+        double* aS = gW + ng;
+        const Arr ar{aS, aS + ng * E, reinterpret_cast<int32_t*>(aS + 2 * ng * E)};
+        int32_t* CNT = ar.tag + ng * E;
+        for (int t = tid; t < ng * E; t += NT) {
+            const int g = t / E, e = t - g * E;
+            const GroupWin* gw = ws.gwin + gb + g;
+            if (e < gw->h) {
+                const double2 v = gw->v[e];
+                ar.S[t] = gS[g] + v.x;
+                ar.W[t] = gW[g] + v.y;
+                ar.tag[t] = gw->tag[e];
             }
         }
-        carry += tot;
+        for (int g = tid; g < ng; g += NT) CNT[g] = ws.gwin[gb + g].h;
+        __syncthreads();
+        merge_arrays<NT>(ar, CNT, ng, E);
+        const int hr = CNT[0];
+        // one root segment per run of a chunk's vertices
+        uint16_t* R16 = reinterpret_cast<uint16_t*>(R);
+        uint32_t* R32 = reinterpret_cast<uint32_t*>(R);
+        int carry = 0;
+        for (int t0 = 0; t0 < hr; t0 += NT) {
+            const int t = t0 + tid;
+            int c = -1;
+            bool st = false, en = false;
+            if (t < hr) {
+                c = tchunk(ar.tag[t]);
+                st = t == 0 || tchunk(ar.tag[t - 1]) != c;
+                en = t == hr - 1 || tchunk(ar.tag[t + 1]) != c;
+            }
+            int tot;
+            const int x = wg_excl_scan_int<NT>(st ? 1 : 0, ired, &tot);
+            const int sidx = carry + x - (st ? 0 : 1);  // this entry's segment
+            if (st) {
+                R32[2 * sidx] = (uint32_t)c;
+                R16[4 * sidx + 2] = (uint16_t)tpos(ar.tag[t]);
+            }
+            if (en) R16[4 * sidx + 3] = (uint16_t)tpos(ar.tag[t]);
+            carry += tot;
+        }
+        nroot = carry;
+    } else {
+        // ---- segment lists over the group hulls' windows
+        int4* D = reinterpret_cast<int4*>(gW + ng);
+        int4* SCR = D + ng;
+        GroupWin* GW = reinterpret_cast<GroupWin*>(SCR + ng);
+        int2* MI = reinterpret_cast<int2*>(GW + ng);
+        int32_t* CNT = reinterpret_cast<int32_t*>(MI + (ng / 2 + 1));
+        int32_t* GH = CNT + ng;
+        {
+            const double2* src = reinterpret_cast<const double2*>(ws.gwin + gb);
+            double2* dst = reinterpret_cast<double2*>(GW);
+            const int nv2 = ng * (int)(sizeof(GroupWin) / sizeof(double2));
+            for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+        }
+        __syncthreads();
+        for (int g = tid; g < ng; g += NT) {
+            GH[g] = GW[g].h;
+            D[g] = make_int4(g, 0, GW[g].h - 1, 0);
+            CNT[g] = 1;
+        }
+        __syncthreads();
+        const size_t sl = (size_t)rb * (kChunk + 1);
+        const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                         ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+        const GroupView X{GW, GH, gS, gW, ws.desc + rb, ws.gpre + rb, ws.cst + rb, Cv, WT};
+        for (int span = 1; span < ng; span <<= 1)
+            merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
+
+        // the root list over groups, expanded into segments of chunk hulls:
+        // first the range of group-list segments each root entry covers, then
+        // one thread per output segment
+        const int nr2 = CNT[0];
+        auto seg_of = [&](int g, int p) {
+            const int base = g * G;
+            int a = 0, b = GW[g].nseg - 1;
+            while (a < b) {
+                const int mid = (a + b + 1) >> 1;
+                if (ws.gpre[rb + base + mid] <= p) a = mid;
+                else b = mid - 1;
+            }
+            return a;
+        };
+        for (int t = tid; t < nr2; t += NT) {
+            const int4 d = D[t];
+            s_ilo[t] = seg_of(d.x, d.y);
+            s_ihi[t] = seg_of(d.x, d.z);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int o = 0;
+            for (int t = 0; t < nr2; ++t) {
+                s_off[t] = o;
+                o += s_ihi[t] - s_ilo[t] + 1;
+            }
+            s_off[nr2] = o;
+        }
+        __syncthreads();
+        nroot = s_off[nr2];
+        for (int o = tid; o < nroot; o += NT) {
+            int a = 0, b = nr2 - 1;
+            while (a < b) {
+                const int mid = (a + b + 1) >> 1;
+                if (s_off[mid] <= o) a = mid;
+                else b = mid - 1;
+            }
+            const int4 dd = D[a];
+            const int i = s_ilo[a] + (o - s_off[a]);
+            const int base = dd.x * G;
+            const uint2 d = ws.desc[rb + base + i];
+            const int pre_i = ws.gpre[rb + base + i];
+            const int lo = i == s_ilo[a] ? dlo(d) + (dd.y - pre_i) : dlo(d);
+            const int hi = i == s_ihi[a] ? dlo(d) + (dd.z - pre_i) : dhi(d);
+            R[o] = mkdesc(dchunk(d), lo, hi);
+        }
     }
     // chunk starts of the row: group start plus the chunk's start in its group
     for (int j = tid; j < m; j += NT) {
@@ -522,12 +653,19 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     }
     __syncthreads();
     if (tid == 0) ws.row_flag[row] = sflag;
-    write_records<NT>(Cv, R, carry, m, ws.vb + rb, ws.rec + rb, ired);
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                     ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+    write_records_scan<NT>(Cv, R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ws.rec + rb, ired);
 }
 
 size_t top_lds_bytes(int ng) {
-    // D, SCR (16 B each), GW, gS, gW (8 B each), MI (8 B per merge), CNT, GH (4 B each)
-    return (size_t)ng * (32 + sizeof(GroupWin) + 16 + 8) + (size_t)(ng / 2 + 1) * 8;
+    // group starts gS, gW (8 B each), then either the segment-list path's D,
+    // SCR (16 B each), GW, MI (8 B per merge), CNT, GH (4 B each), or the
+    // compact-array path's 2 kWinK entries per group (S, W, tag) and CNT
+    const size_t gen = (size_t)ng * (32 + sizeof(GroupWin) + 8) + (size_t)(ng / 2 + 1) * 8;
+    const size_t fast = (size_t)ng * (2 * kGWinK) * 20 + (size_t)ng * 4;
+    return (size_t)ng * 16 + (gen > fast ? gen : fast);
 }
 
 }  // namespace
