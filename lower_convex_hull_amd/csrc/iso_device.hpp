@@ -183,7 +183,7 @@ struct List {
 // false then true along the range and true at Y: bisection over segments (by
 // each segment's last in-range vertex), then within one segment.
 template <class DT, class F>
-__device__ Cur find_first(const List<DT> Lst, Cur X, Cur Y, F pred) {
+__device__ __forceinline__ Cur find_first(const List<DT> Lst, Cur X, Cur Y, F pred) {
     int lo = X.seg, hi = Y.seg;
     while (lo < hi) {
         int mid = (lo + hi) >> 1;
@@ -405,7 +405,7 @@ __device__ __forceinline__ void keep(double v) { asm volatile("" ::"v"(v)); }
 // and the slopes of the edges into and out of it, or the one edge it lies
 // under; and the number of root vertices before it (for block ids).
 template <int NT>
-__device__ void write_records(const RowView X, const uint2* D, int nroot, int m, int32_t* vb,
+__device__ __forceinline__ void write_records(const RowView X, const uint2* D, int nroot, int m, int32_t* vb,
                               ChunkRec* rec, int* ired) {
     const int tid = threadIdx.x;
     int carry = 0;
@@ -628,7 +628,7 @@ __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r
 // a+span merge into node a, one wave per merge.  Leaves the root's hull in
 // entries 0..cnt[0]-1.
 template <int NT>
-__device__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn, int E) {
+__device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn, int E) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     for (int span = 1; span < nn; span <<= 1) {
@@ -644,14 +644,13 @@ __device__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn, int E) {
     }
 }
 
-// Reconstruction records (Corollary 4.5) from a root list of nroot segments
-// D (LDS or workspace), at most one per chunk and in chunk order.  Per chunk
-// j, the index of the first segment whose chunk is >= j is the number of
-// segments in earlier chunks: a scan over the chunks (in fs, m ints)
-// instead of a search per chunk.
+// Prefix counts over a row's root list D of nroot segments (at most one per
+// chunk, in chunk order) for the reconstruction: vb[i] = root vertices before
+// segment i (block ids), and fs[j] = segments in chunks before chunk j, which
+// is the index of the first segment whose chunk is >= j.
 template <int NT>
-__device__ void write_records_scan(const RowView X, const uint2* D, int nroot, int m, int32_t* vb,
-                                   int32_t* fs, ChunkRec* rec, int* ired) {
+__device__ __forceinline__ void root_prefixes(const uint2* D, int nroot, int m, int32_t* vb, int32_t* fs,
+                                              int* ired) {
     const int tid = threadIdx.x;
     for (int j = tid; j < m; j += NT) fs[j] = 0;
     __syncthreads();
@@ -676,41 +675,47 @@ __device__ void write_records_scan(const RowView X, const uint2* D, int nroot, i
         vcarry += tot;
     }
     __syncthreads();
-    for (int j = tid; j < m; j += NT) {
-        const int i = fs[j];  // first root segment with chunk >= j
-        const uint2 d = D[min(i, nroot - 1)];
-        ChunkRec rc;
-        rc.pad = 0;
-        if (i < nroot && dchunk(d) == j) {
-            rc.vb = vb[i];
-            rc.lo = dlo(d);
-            rc.hi = dhi(d);
-            rc.slope_in = 0.0;
-            rc.slope_out = 0.0;
-            if (i > 0) {
-                const uint2 p = D[i - 1];
-                const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
-                rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
-            }
-            if (i + 1 < nroot) {
-                const uint2 q = D[i + 1];
-                const Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
-                rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
-            }
-        } else {
-            // the chunk lies under one edge, from the last vertex of the
-            // previous segment to the first vertex of the next (chunk 0
-            // always holds the row's first point, so i >= 1)
+}
+
+// The reconstruction record of chunk j (Corollary 4.5) from the root list and
+// its prefix counts: the range of the chunk's surviving hull vertices and the
+// slopes of the edges into and out of it, or the one edge it lies under.
+__device__ __forceinline__ ChunkRec chunk_record(const RowView X, const uint2* D, int nroot,
+                                                 const int32_t* vb, const int32_t* fs, int j) {
+    const int i = fs[j];  // first root segment with chunk >= j
+    const uint2 d = D[min(i, nroot - 1)];
+    ChunkRec rc;
+    rc.pad = 0;
+    if (i < nroot && dchunk(d) == j) {
+        rc.vb = vb[i];
+        rc.lo = dlo(d);
+        rc.hi = dhi(d);
+        rc.slope_in = 0.0;
+        rc.slope_out = 0.0;
+        if (i > 0) {
             const uint2 p = D[i - 1];
-            const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
-            rc.vb = vb[i];
-            rc.lo = -1;
-            rc.hi = -1;
+            const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
             rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
-            rc.slope_out = rc.slope_in;
         }
-        rec[j] = rc;
+        if (i + 1 < nroot) {
+            const uint2 q = D[i + 1];
+            const Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
+            rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
+        }
+    } else {
+        // the chunk lies under one edge, from the last vertex of the previous
+        // segment to the first vertex of the next (chunk 0 always holds the
+        // row's first point, so i >= 1; the last chunk holds its last point,
+        // so i < nroot)
+        const uint2 p = D[i - 1];
+        const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
+        rc.vb = vb[i];
+        rc.lo = -1;
+        rc.hi = -1;
+        rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+        rc.slope_out = rc.slope_in;
     }
+    return rc;
 }
 
 }  // namespace

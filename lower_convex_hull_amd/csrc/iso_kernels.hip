@@ -95,7 +95,7 @@ struct HullOut {
 // applied, sanitised) in yv and its points' S (and W) in ps/pw: ps[b] is point
 // base+b+1.
 template <int NT, int P, bool WT>
-__device__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
+__device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
                               const float* __restrict__ gw, int len, float sign, float (&yv)[P],
                               double (&ps)[P], double (&pw)[P], double& s0, double& w0) {
     constexpr int RS = P + 1;
@@ -519,11 +519,12 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
 template <bool WT>
 __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
                                                     float* __restrict__ out,
-                                                    int32_t* __restrict__ block_id) {
+                                                    int32_t* __restrict__ block_id, int rec_done) {
     constexpr int NT = kLongNT, C = kChunk;
     constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
     __shared__ int vidx[C + 1];
     __shared__ float vslope[C + 1];
+    __shared__ ChunkRec s_rc;
     const int64_t gid = blockIdx.x;
     const int64_t row = gid / m;
     const int j = (int)(gid - row * m);
@@ -556,7 +557,20 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         }
         return;
     }
-    const ChunkRec rc = ws.rec[gid];
+    if (tid == 0) {
+        if (rec_done) {
+            s_rc = ws.rec[gid];
+        } else {
+            // this chunk's record from the row's root list (Corollary 4.5)
+            const int64_t rb = row * m;
+            const size_t sl = (size_t)rb * (C + 1);
+            const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                            ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+            s_rc = chunk_record(X, ws.desc_scr + rb, ws.root_n[row], ws.vb + rb, ws.node_cnt + rb, j);
+        }
+    }
+    __syncthreads();
+    const ChunkRec rc = s_rc;
     if (rc.lo < 0) {
         const float v = sign * (float)rc.slope_in;
         const int b = rc.vb - 1;
@@ -639,15 +653,16 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
         hipLaunchKernelGGL(k_chunk_hulls<false>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
                            sh.sign, ws);
     timed_end(st);
-    hipError_t e = copy_control ? launch_copy_merge(sh, ws, st) : launch_segment_merge(sh, ws, st);
+    bool rec_done = true;
+    hipError_t e = copy_control ? launch_copy_merge(sh, ws, st) : launch_segment_merge(sh, ws, st, &rec_done);
     if (e != hipSuccess) return e;
     timed_begin(kPhaseExpand, st);
     if (wt)
         hipLaunchKernelGGL(k_expand<true>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign, ws,
-                           out, block_id);
+                           out, block_id, (int)rec_done);
     else
         hipLaunchKernelGGL(k_expand<false>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign,
-                           ws, out, block_id);
+                           ws, out, block_id, (int)rec_done);
     timed_end(st);
     return hipGetLastError();
 }

@@ -94,6 +94,7 @@ struct LongWs {
     double2* gtot;        // [R*ng] group totals (S, W)
     double2* cst;         // [R*m] chunk starts relative to their group's start
     int32_t* gpre;        // [R*m] vertices before each segment of a group's list
+    int32_t* root_n;      // [R] segments in the root list (desc_scr) of each row
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
@@ -129,9 +130,11 @@ void timed_end(hipStream_t st);
 hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                         float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
 
-// The merge phase over segment lists (iso_merge.hip); leaves the
-// reconstruction records in ws.rec.
-hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
+// The merge phase over segment lists (iso_merge.hip).  Leaves either the
+// reconstruction records in ws.rec (*rec_done = true) or each row's root list
+// in ws.desc_scr with its prefix counts, from which the expansion computes
+// the records (*rec_done = false).
+hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done);
 
 // The merge phase of the vertex-copying control (iso_copy.hip); leaves the
 // reconstruction records in ws.rec like the segment-list merge.

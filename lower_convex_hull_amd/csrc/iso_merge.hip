@@ -472,11 +472,18 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         int f = 0;
         for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
         if (f) atomicOr(&sflag, f);
-        const RowView Xr{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
-                         lS, lW, WT};
-        write_records_scan<NT>(Xr, D, nseg, m, ws.vb + rb, sfirst, ws.rec + rb, ired);
-        __syncthreads();
-        if (tid == 0) ws.row_flag[row] = sflag;
+        // the root list, its prefix counts and the chunk starts, for the
+        // expansion's records
+        for (int i = tid; i < nseg; i += NT) ws.desc_scr[rb + i] = D[i];
+        for (int j = tid; j < m; j += NT) {
+            ws.st_S[rb + j] = lS[j];
+            if (WT) ws.st_W[rb + j] = lW[j];
+        }
+        root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired);
+        if (tid == 0) {
+            ws.row_flag[row] = sflag;
+            ws.root_n[row] = nseg;
+        }
     }
 }
 
@@ -652,11 +659,12 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         if (WT) ws.st_W[rb + j] = gW[j / G] + c.y;
     }
     __syncthreads();
-    if (tid == 0) ws.row_flag[row] = sflag;
-    const size_t sl = (size_t)rb * (kChunk + 1);
-    const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
-                     ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
-    write_records_scan<NT>(Cv, R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ws.rec + rb, ired);
+    // prefix counts of the root list for the expansion's records
+    root_prefixes<NT>(R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ired);
+    if (tid == 0) {
+        ws.row_flag[row] = sflag;
+        ws.root_n[row] = nroot;
+    }
 }
 
 size_t top_lds_bytes(int ng) {
@@ -679,11 +687,12 @@ size_t merge_lds_bytes(int m, bool weighted) {
 
 // The merge phase over segment lists: one workgroup per row, lists in LDS when
 // they fit.
-hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st) {
+hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
     const bool wt = sh.weighted;
     const int ng = (sh.m + kGroup - 1) / kGroup;
     const unsigned R = (unsigned)sh.rows;
     if (ng <= kTopMax) {
+        *rec_done = false;
         timed_begin(kPhaseMerge, st);
         if (wt)
             hipLaunchKernelGGL(k_group_merge<true>, dim3(R * (unsigned)ng), dim3(kGroupNT), 0, st, sh.m,
@@ -714,6 +723,7 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     }
     // very long rows: one workgroup per row merges every level, lists in the
     // workspace
+    *rec_done = true;
     timed_begin(kPhaseMerge, st);
     if (wt)
         hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);

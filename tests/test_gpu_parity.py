@@ -185,6 +185,33 @@ def test_long_walks_and_bisection(torch):
         check(torch, y, w, name=f"cliffs-w/{n}")
 
 
+def test_mixed_dense_and_noisy_stretches(torch):
+    """One row whose groups of chunk hulls are partly short (noise) and partly
+    long (strictly increasing stretches), so the short-hull and the
+    segment-list merge paths meet in one row and in its top stage."""
+    rng = np.random.default_rng(31)
+    parts = []
+    for k in range(8):
+        seg = 300_000
+        if k % 2 == 0:
+            d, _ = inputs.dense(seg, 32 + k)
+            parts.append(d[0] * 2.0 + k * 0.25)
+        else:
+            parts.append((np.linspace(0, 3, seg) + rng.standard_normal(seg)).astype(np.float32) * 0.5 + k * 0.25)
+    y = np.concatenate(parts).astype(np.float32)[None, :]
+    check(torch, y, None, name="mixed/2.4e6", block_ids=False)
+    w = inputs.weights("exp", y.shape[1], 33)[None, :]
+    check(torch, y, w, name="mixed-w/2.4e6", block_ids=False)
+
+
+def test_row_beyond_two_stage_merge(torch):
+    """A row with more groups than the two-stage merge keeps in LDS: one
+    workgroup merges every level with its lists in the workspace."""
+    n = 96 * 64 * 4096 + 12345
+    y, _ = inputs.noisy(1, n, 34)
+    check(torch, y, None, name="noisy/2.5e7", block_ids=False)
+
+
 def test_sawtooth_and_walk_families_at_1e6(torch):
     for fam in ("sawtooth", "random_walk", "cliff", "piecewise"):
         y = inputs.family(fam, 1_000_000, 24)[None, :]
