@@ -68,7 +68,7 @@ __global__ __launch_bounds__(1024) void k_cp_setup(int m, LongWs ws) {
     if (tid == 0) sflag = 0;
     __syncthreads();
     int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
     if (f) atomicOr(&sflag, f);
     double cS = 0.0, cW = 0.0;
     int cO = 0;

@@ -116,6 +116,26 @@ struct Cur {
     int pos;
 };
 
+// Where the points of a strictly increasing chunk (chunk flag kChunkInc) come
+// from: the chunk's elements and its per-thread checkpoints.
+struct IncSrc {
+    const int32_t* cflag;  // chunk flags of the row (null: every chunk has a slot)
+    const double* ckS;     // checkpoints of the row's chunks, kLongNT + 1 each
+    const double* ckW;
+    const float* y;        // the row's elements
+    const float* w;
+    float sign;
+};
+
+// ... for the chunks j0, j0+1, ... of a row (chunk j0 is chunk 0 of the view)
+__device__ __forceinline__ IncSrc inc_src(const LongWs& ws, int64_t row, int m, int j0) {
+    const int64_t cb = row * m + j0;
+    const int64_t eb = row * ws.n + (int64_t)j0 * kChunk;
+    return IncSrc{ws.chunk_flag + cb, ws.ck_S + cb * (kLongNT + 1),
+                  ws.ck_W ? ws.ck_W + cb * (kLongNT + 1) : nullptr, ws.y + eb,
+                  ws.w ? ws.w + eb : nullptr, ws.sign};
+}
+
 struct RowView {
     const uint16_t* idx;  // full slots (rarely read)
     const double* S;
@@ -125,9 +145,46 @@ struct RowView {
     const double* stS;    // chunk starts
     const double* stW;
     bool weighted;
+    IncSrc inc;
+
+    // Point k of strictly increasing chunk j (chunk-relative), summed exactly
+    // as the chunk kernel summed it: its thread's checkpoint plus that
+    // thread's elements up to the point, in order.
+    __device__ __forceinline__ Pt inc_point(int j, int k) const {
+        constexpr int P = kLongP;
+        Pt p;
+        if (k == 0) return Pt{0.0, 0.0};
+        const int L = (k - 1) / P, b = (k - 1) - L * P;
+        const size_t c = (size_t)j * (kLongNT + 1) + L;
+        if (b == P - 1) {
+            p.s = inc.ckS[c + 1];
+            p.w = weighted ? inc.ckW[c + 1] : (double)k;
+            return p;
+        }
+        const float* gy = inc.y + (int64_t)j * kChunk + L * P;
+        const float* gw = weighted ? inc.w + (int64_t)j * kChunk + L * P : nullptr;
+        double ls = 0.0, lw = 0.0;
+        for (int t = 0; t <= b; ++t) {
+            float yy = gy[t];
+            if (!isfinite(yy)) yy = 0.0f;
+            const float yv = inc.sign * yy;
+            if (weighted) {
+                float ww = gw[t];
+                if (!(ww > 0.0f && isfinite(ww))) ww = 1.0f;
+                ls += (double)ww * (double)yv;
+                lw += (double)ww;
+            } else {
+                ls += (double)yv;
+            }
+        }
+        p.s = inc.ckS[c] + ls;
+        p.w = weighted ? inc.ckW[c] + lw : (double)k;
+        return p;
+    }
 
     // Vertex `pos` of chunk j's hull in chunk-relative coordinates: from the
-    // compact window when it holds it, else from the full slot.
+    // compact window when it holds it, else from the full slot (or, for a
+    // strictly increasing chunk, from its elements).
     __device__ __forceinline__ Pt vrel(int j, int pos) const {
         const int h = hc[j];
         int e = pos;
@@ -137,6 +194,8 @@ struct RowView {
             const double2 v = win[j].v[e];
             p.s = v.x;
             p.w = v.y;
+        } else if (inc.cflag && (inc.cflag[j] & kChunkInc)) {
+            p = inc_point(j, pos);
         } else {
             const size_t o = (size_t)j * (kChunk + 1) + pos;
             p.s = S[o];

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
 template <bool WT>
 __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict__ y,
                                                          const float* __restrict__ w, int64_t n,
-                                                         int m, float sign, LongWs ws) {
+                                                         int m, float sign, LongWs ws, int full_slots) {
     constexpr int NT = kLongNT, P = kLongP, C = kChunk;
     __shared__ HullSmem<NT, P, WT> sm;
     const int64_t gid = blockIdx.x;  // row * m + chunk
@@ -469,7 +469,28 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
         if (h <= 2 * kWinK || r < kWinK) return r;
         return r >= h - kWinK ? kWinK + r - (h - kWinK) : -1;
     };
-    if (ho.all) {
+    int cflag = sm.flag;
+    if (ho.all && !full_slots) {
+        // every point 0..len is a vertex, at its own index: no slot; the
+        // window, and each thread's first S (and W) as a checkpoint from which
+        // a point is recomputed (with the chunk end as the last checkpoint)
+        double* ck = ws.ck_S + (size_t)gid * (NT + 1);
+        ck[L] = s0;
+        if (L == NT - 1) ck[NT] = ps[P - 1];
+        if (WT) {
+            double* cw = ws.ck_W + (size_t)gid * (NT + 1);
+            cw[L] = w0;
+            if (L == NT - 1) cw[NT] = pw[P - 1];
+        }
+        if (L == 0) wr->v[0] = make_double2(0.0, 0.0);
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            const int k = base + b + 1;
+            const int e = k <= len ? wslot(k) : -1;
+            if (e >= 0) wr->v[e] = make_double2(ps[b], WT ? pw[b] : (double)k);
+        }
+        cflag |= kChunkInc;
+    } else if (ho.all) {
         // every point 0..len is a vertex: stage the points' S (and W) in LDS
         // (point k at k + (k-1)/P, so that threads writing their own points hit
         // different banks), then write the slot with consecutive threads on
@@ -508,7 +529,7 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
         ws.hull_cnt[gid] = h;
         ws.tot_S[gid] = sm.end_s;
         if (WT) ws.tot_W[gid] = sm.end_w;
-        ws.chunk_flag[gid] = sm.flag;
+        ws.chunk_flag[gid] = cflag;
     }
 }
 
@@ -525,6 +546,7 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
     __shared__ int vidx[C + 1];
     __shared__ float vslope[C + 1];
     __shared__ ChunkRec s_rc;
+    __shared__ int s_inc;
     const int64_t gid = blockIdx.x;
     const int64_t row = gid / m;
     const int j = (int)(gid - row * m);
@@ -565,9 +587,11 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
             const int64_t rb = row * m;
             const size_t sl = (size_t)rb * (C + 1);
             const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
-                            ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+                            ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
+                            inc_src(ws, row, m, 0)};
             s_rc = chunk_record(X, ws.desc_scr + rb, ws.root_n[row], ws.vb + rb, ws.node_cnt + rb, j);
         }
+        s_inc = (ws.chunk_flag[gid] & kChunkInc) != 0;
     }
     __syncthreads();
     const ChunkRec rc = s_rc;
@@ -581,6 +605,37 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         return;
     }
     const int nv = rc.hi - rc.lo + 1;
+    if (s_inc) {
+        // every point of the chunk is a vertex at its own index: an element
+        // between two surviving vertices is its own edge, so its fit is its
+        // value; elements before or after the surviving range take the edges
+        // into and out of it
+        const float* gy = ws.y + off;
+        const bool vy = vec && (((uintptr_t)gy) & 15u) == 0;
+        const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
+        for (int g = 0; g < G; ++g) {
+            const int e0 = 4 * (g * NT + tid);
+            if (e0 >= len) break;
+            float yy[4];
+            if (vy && e0 + 4 <= len) {
+                const float4 v = *reinterpret_cast<const float4*>(gy + e0);
+                yy[0] = v.x; yy[1] = v.y; yy[2] = v.z; yy[3] = v.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) yy[t] = e0 + t < len ? gy[e0 + t] : 0.0f;
+            }
+            float vv[4];
+            int bb[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = e0 + t;
+                vv[t] = e < rc.lo ? sin_ : (e >= rc.hi ? sout : yy[t]);
+                bb[t] = rc.vb + (e < rc.lo ? 0 : min(e - rc.lo + 1, nv)) - 1;
+            }
+            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+        }
+        return;
+    }
     const size_t slot = (size_t)gid * (C + 1) + rc.lo;
     for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
     for (int v = tid; v + 1 < nv; v += NT) {
@@ -641,17 +696,24 @@ hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n,
     return launch_short_t<256, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
 }
 
-hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
+hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws0,
                        float* out, int32_t* block_id, bool copy_control, hipStream_t st) {
     const unsigned nblk = (unsigned)(sh.rows * sh.m);
     const bool wt = sh.weighted;
+    LongWs ws = ws0;
+    ws.y = y;
+    ws.w = w;
+    ws.n = sh.n;
+    ws.sign = sh.sign;
+    // the copy control reads every chunk hull from its slot
+    const int full_slots = copy_control ? 1 : 0;
     timed_begin(kPhaseChunk, st);
     if (wt)
         hipLaunchKernelGGL(k_chunk_hulls<true>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
-                           sh.sign, ws);
+                           sh.sign, ws, full_slots);
     else
         hipLaunchKernelGGL(k_chunk_hulls<false>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
-                           sh.sign, ws);
+                           sh.sign, ws, full_slots);
     timed_end(st);
     bool rec_done = true;
     hipError_t e = copy_control ? launch_copy_merge(sh, ws, st) : launch_segment_merge(sh, ws, st, &rec_done);

@@ -31,6 +31,11 @@ constexpr int kHardCap = 256;     // merges per level a wave may take over
 // Per-row data flags written by the kernels (read back by the checking path).
 constexpr int kFlagNonfinite = 1;
 constexpr int kFlagWeight = 2;
+constexpr int kFlagData = kFlagNonfinite | kFlagWeight;
+// Chunk flag: the chunk's elements strictly increase, so every point is a
+// hull vertex (position = point index) and the chunk's slot is not written;
+// its points are recomputed from the input and the per-thread checkpoints.
+constexpr int kChunkInc = 4;
 
 // Reconstruction record of one chunk, written by the merge phase.
 //   lo < 0: no vertex of the row's hull lies in the chunk; every element of
@@ -95,6 +100,13 @@ struct LongWs {
     double2* cst;         // [R*m] chunk starts relative to their group's start
     int32_t* gpre;        // [R*m] vertices before each segment of a group's list
     int32_t* root_n;      // [R] segments in the root list (desc_scr) of each row
+    double* ck_S;         // [R*m*(kLongNT+1)] S at each thread's first point (and the chunk end)
+    double* ck_W;         // (weighted only)
+    // the call's inputs, for points recomputed from them
+    const float* y;
+    const float* w;
+    int64_t n;
+    float sign;
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     if (tid == 0) sflag = 0;
     __syncthreads();
     int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
     if (f) atomicOr(&sflag, f);
     double carryS = 0.0, carryW = 0.0;
     for (int t0 = 0; t0 < m; t0 += NT) {
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
 
     const size_t sl = (size_t)rb * (kChunk + 1);
     RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
-              STS, WT ? STW : nullptr, WT};
+              STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
 
     // ---- the merge tree, level by level
     for (int span = 1; span < m; span <<= 1) {
@@ -422,7 +422,8 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             CNT[i] = 1;
         }
         __syncthreads();
-        const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT};
+        const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT,
+                        inc_src(ws, row, m, j0)};
         for (int span = 1; span < gc; span <<= 1)
             merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
         nseg = CNT[0];
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         if (tid == 0) sflag = 0;
         __syncthreads();
         int f = 0;
-        for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+        for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
         if (f) atomicOr(&sflag, f);
         // the root list, its prefix counts and the chunk starts, for the
         // expansion's records
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     if (tid == 0) sflag = 0;
     __syncthreads();
     int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j];
+    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
     if (f) atomicOr(&sflag, f);
 
     // group starts (exclusive scan of the group totals)
@@ -600,7 +601,8 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         __syncthreads();
         const size_t sl = (size_t)rb * (kChunk + 1);
         const RowView Cv{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
-                         ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT};
+                         ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
+                         inc_src(ws, row, m, 0)};
         const GroupView X{GW, GH, gS, gW, ws.desc + rb, ws.gpre + rb, ws.cst + rb, Cv, WT};
         for (int span = 1; span < ng; span <<= 1)
             merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
