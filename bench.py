@@ -202,7 +202,7 @@ def main():
 
     # ---- roofline of the dominant kernel
     per_elem_bytes = {"chunk_hulls": 4, "expand": 4, "short_rows": 8, "merge": 0, "merge_top": 0,
-                      "copy_bridge": 0, "copy_move": 0}
+                      "copy_bridge": 0, "copy_move": 0, "chunk_redo": 0}
     weighted = any(j["w"] is not None for j in jobs)
     if weighted:
         per_elem_bytes.update(chunk_hulls=8, short_rows=12)

@@ -151,7 +151,8 @@ enum {
     ISO_PHASE_COPY_BRIDGE = 4, /* copy control: bridges of one level      */
     ISO_PHASE_COPY_MOVE = 5,   /* copy control: vertex rewrite of a level */
     ISO_PHASE_MERGE_TOP = 6,   /* second merge stage (group hulls of a row) */
-    ISO_PHASE_COUNT = 7
+    ISO_PHASE_CHUNK_REDO = 7,  /* chunk hulls the first chunk kernel left over */
+    ISO_PHASE_COUNT = 8
 };
 int iso_timing_enable(int on);
 int iso_timing_read(double* ms, int64_t* launches, int nphase);

@@ -43,19 +43,33 @@ namespace {
 // thus holds its hull at the start of its first thread's region, and the
 // workgroup's hull ends up at the start of region 0.
 // ----------------------------------------------------------------------------
-template <int NT, int P, bool WT>
+// How a workgroup builds its hull: quickhull, then chains and merges if
+// quickhull gives up (short rows); quickhull only, leaving a chunk it gives up
+// on for the fallback kernel; or chains and merges only (that fallback).
+constexpr int kHullBoth = 0, kHullQuick = 1, kHullChains = 2;
+
+template <int NT, int P, bool WT, int MODE>
 struct HullSmem {
     static constexpr int RS = P + 1;
-    double S[NT * RS];           // block-relative S of each array entry
-    double W[WT ? NT * RS : 1];  // block-relative W (weighted; else W is the index)
-    uint16_t idx[NT * RS];       // block point index of each entry
-    int32_t cnt[NT];             // entries of the node stored from this region
-    int32_t mvk[NT];             // per merge: kept entries of the left array
-    int32_t mvb[NT];             // per merge: first kept entry of the right array
+    static constexpr int NR = MODE == kHullQuick ? 1 : NT * RS;  // region entries
+    static constexpr int NQ = MODE == kHullChains ? 1 : kQhMax;  // quickhull entries
+    double S[NR];                 // block-relative S of each array entry
+    double W[WT ? NR : 1];        // block-relative W (weighted; else W is the index)
+    uint16_t idx[NR];             // block point index of each entry
+    int32_t cnt[MODE == kHullQuick ? 1 : NT];  // entries of the node stored from this region
+    int32_t mvk[MODE == kHullQuick ? 1 : NT];  // per merge: kept entries of the left array
+    int32_t mvb[MODE == kHullQuick ? 1 : NT];  // per merge: first kept entry of the right array
     double red[NT / 64 + 1];
     int ired[NT / 64 + 1];
-    double end_s, end_w;         // S and W of point len (padding points repeat it)
+    double end_s, end_w;          // S and W of point len (padding points repeat it)
     int flag;
+    // quickhull: the vertex list (two buffers), and per chord the key of the
+    // farthest point below it and that point's coordinates
+    int32_t qk[2][NQ];
+    double qS[2][NQ], qW[2][NQ];
+    unsigned long long qkey[NQ];
+    double qnS[NQ], qnW[NQ];
+    int qn, qcur, qstate;
 };
 
 // Exclusive and inclusive workgroup scans of one f64 value per thread.  The
@@ -83,19 +97,22 @@ __device__ __forceinline__ void wg_scan2(double v, double* red, double& excl, do
     incl = before + x;
 }
 
-// Result of block_hull: either every point 0..len is a vertex (`all`), or the
-// hull's h vertices are entries 0..h-1 of the LDS arrays.
+// Result of block_hull: every point 0..len is a vertex (`all`); or the hull's
+// h vertices are entries 0..h-1 of the region arrays, or (quickhull-only
+// mode) of the quickhull list qk/qS/qW[qcur]; or (quickhull-only mode) the
+// block needs the fallback (`fail`).
 struct HullOut {
     bool all;
     int h;
+    bool fail;
 };
 
 // Loads the block's elements, forms the block-relative cumulative sums, and
 // builds the block's lower hull.  Returns this thread's element values (sign
 // applied, sanitised) in yv and its points' S (and W) in ps/pw: ps[b] is point
 // base+b+1.
-template <int NT, int P, bool WT>
-__device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const float* __restrict__ gy,
+template <int NT, int P, bool WT, int MODE>
+__device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, const float* __restrict__ gy,
                               const float* __restrict__ gw, int len, float sign, float (&yv)[P],
                               double (&ps)[P], double (&pw)[P], double& s0, double& w0) {
     constexpr int RS = P + 1;
@@ -202,7 +219,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const flo
         for (int b = 0; b < P; ++b)
             if (base + b + 1 > len) { ps[b] = es; if (WT) pw[b] = ew; }
     }
-    if (all) return HullOut{true, len + 1};
+    if (all) return HullOut{true, len + 1, false};
 
     // ---- candidates: point k is a vertex only if the slope into it (element
     // k-1) is below the slope out of it (element k).  Points next to a padding
@@ -225,6 +242,202 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const flo
         return p;
     };
 
+    // ---- quickhull first: every chord of the current vertex list takes the
+    // point farthest below it as a new vertex, and a point on or above its
+    // chord is dropped, until no point is left.  Noise-like blocks finish in
+    // a few levels with few vertices; a block that needs more levels or more
+    // vertices falls back to the chains and merges below.
+    if constexpr (MODE != kHullChains) {
+        uint32_t alive = 0;
+#pragma unroll
+        for (int b = 0; b < P; ++b)
+            if (((cand >> (b + 1)) & 1u) && base + b + 1 < len) alive |= 1u << b;
+        if (L == 0) {
+            sm.qk[0][0] = 0;
+            sm.qS[0][0] = 0.0;
+            sm.qW[0][0] = 0.0;
+            sm.qk[0][1] = len;
+            sm.qS[0][1] = sm.end_s;
+            sm.qW[0][1] = sm.end_w;
+            sm.qn = 2;
+            sm.qcur = 0;
+            sm.qstate = 0;
+        }
+        if (L < kQhMax) sm.qkey[L] = 0ull;
+        __syncthreads();
+        for (int lv = 0; lv < kQhLevels; ++lv) {
+            const int cb = sm.qcur, nv = sm.qn;
+            const int32_t* vk = sm.qk[cb];
+            // the chord over this thread's first point: vk[i0] <= base < vk[i0+1]
+            int i0 = 0;
+            if (alive) {
+                int hi = nv - 1;
+                while (hi - i0 > 1) {
+                    const int mid = (i0 + hi) >> 1;
+                    if (vk[mid] <= base) i0 = mid;
+                    else hi = mid;
+                }
+            }
+            int qi = 0;                 // this thread's last chord
+            unsigned long long qbest = 0ull;  // and its best key there
+            if (alive) {
+                // chord i runs from vertex vk[i] to vertex nk = vk[i+1]; reloaded
+                // only when this thread's points pass a vertex
+                int i = i0, nk = vk[i0 + 1];
+                Pt A{sm.qW[cb][i0], sm.qS[cb][i0]}, B{sm.qW[cb][i0 + 1], sm.qS[cb][i0 + 1]};
+                unsigned long long best = 0ull;
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    if (!((alive >> b) & 1u)) continue;
+                    const int k = base + b + 1;
+                    if (k >= nk) {
+                        if (best) atomicMax(&sm.qkey[i], best);
+                        best = 0ull;
+                        do {
+                            ++i;
+                            nk = vk[i + 1];
+                        } while (nk <= k);
+                        A = Pt{sm.qW[cb][i], sm.qS[cb][i]};
+                        B = Pt{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
+                    }
+                    const Pt Pk{WT ? pw[b] : (double)k, ps[b]};
+                    const double c = cross3(A, Pk, B);
+                    if (c > 0.0) {
+                        // the farthest point below the chord, the lowest index on a tie
+                        // (the low 13 bits of the positive f64 give way to the index)
+                        const unsigned long long key =
+                            ((unsigned long long)__double_as_longlong(c) & ~0x1fffull) |
+                            (unsigned long long)(0x1fff - k);
+                        best = key > best ? key : best;
+                    } else {
+                        alive &= ~(1u << b);
+                    }
+                }
+                qi = i;
+                qbest = best;
+            }
+            {
+                // one atomic per wave when all of its threads with a candidate
+                // ended on the same chord (always so at the first level)
+                const uint64_t act = __ballot(qbest != 0ull);
+                if (act) {
+                    const int lane = threadIdx.x & 63;
+                    const int first = __ffsll((long long)act) - 1;
+                    const int fi = __shfl(qi, first);
+                    if (__ballot(qbest != 0ull && qi != fi) == 0) {
+                        unsigned long long mx = qbest;
+#pragma unroll
+                        for (int d = 1; d < 64; d <<= 1) {
+                            const unsigned long long o = __shfl_xor(mx, d);
+                            mx = o > mx ? o : mx;  // threads without a candidate hold 0
+                        }
+                        if (lane == first) atomicMax(&sm.qkey[fi], mx);
+                    } else if (qbest) {
+                        atomicMax(&sm.qkey[qi], qbest);
+                    }
+                }
+            }
+            __syncthreads();
+            // the winners write their coordinates for the new vertex list
+            if (alive) {
+                int i = i0, nk = vk[i0 + 1];
+                int win = (int)(0x1fff - (sm.qkey[i0] & 0x1fffull));
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    if (!((alive >> b) & 1u)) continue;
+                    const int k = base + b + 1;
+                    if (k >= nk) {
+                        do {
+                            ++i;
+                            nk = vk[i + 1];
+                        } while (nk <= k);
+                        win = (int)(0x1fff - (sm.qkey[i] & 0x1fffull));
+                    }
+                    if (win == k) {
+                        sm.qnS[i] = ps[b];
+                        sm.qnW[i] = WT ? pw[b] : (double)k;
+                        alive &= ~(1u << b);
+                    }
+                }
+            }
+            __syncthreads();
+            if (L < 64) {
+                // one wave inserts the new vertices after their chords' starts
+                const bool found = L < nv - 1 && sm.qkey[L] != 0ull;
+                const uint64_t bal = __ballot(found);
+                const int pre = __popcll(bal & ((1ull << L) - 1ull));
+                const int add = __popcll(bal);
+                const int nb = 1 - cb;
+                if (nv + add <= kQhMax && L < nv) {
+                    sm.qk[nb][L + pre] = vk[L];
+                    sm.qS[nb][L + pre] = sm.qS[cb][L];
+                    sm.qW[nb][L + pre] = sm.qW[cb][L];
+                    if (found) {
+                        sm.qk[nb][L + pre + 1] = (int)(0x1fff - (sm.qkey[L] & 0x1fffull));
+                        sm.qS[nb][L + pre + 1] = sm.qnS[L];
+                        sm.qW[nb][L + pre + 1] = sm.qnW[L];
+                    }
+                }
+                if (L < kQhMax) sm.qkey[L] = 0ull;
+                if (L == 0) {
+                    if (add == 0) {
+                        sm.qstate = 1;  // no point left below any chord: done
+                    } else if (nv + add > kQhMax) {
+                        sm.qstate = 2;  // too many vertices: fall back
+                    } else {
+                        sm.qn = nv + add;
+                        sm.qcur = nb;
+                    }
+                }
+            }
+            __syncthreads();
+            if (sm.qstate != 0) break;
+        }
+        if (sm.qstate == 1) {
+            // the vertex list, made convex as computed (a near-tie may have
+            // picked a point that is not quite the farthest)
+            const int cb = sm.qcur, nv = sm.qn;
+            if (L < 64) {
+                bool ok = true;
+                if (L >= 1 && L + 1 < nv)
+                    ok = cross3(Pt{sm.qW[cb][L - 1], sm.qS[cb][L - 1]}, Pt{sm.qW[cb][L], sm.qS[cb][L]},
+                                Pt{sm.qW[cb][L + 1], sm.qS[cb][L + 1]}) > 0.0;
+                if (__ballot(!ok) != 0 && L == 0) {
+                    // a monotone chain over the list, into the other buffer
+                    const int nb = 1 - cb;
+                    int dep = 0;
+                    for (int t = 0; t < nv; ++t) {
+                        const Pt Cp{sm.qW[cb][t], sm.qS[cb][t]};
+                        while (dep >= 2 && cross3(Pt{sm.qW[nb][dep - 2], sm.qS[nb][dep - 2]},
+                                                  Pt{sm.qW[nb][dep - 1], sm.qS[nb][dep - 1]}, Cp) <= 0.0)
+                            --dep;
+                        sm.qS[nb][dep] = Cp.s;
+                        sm.qW[nb][dep] = Cp.w;
+                        sm.qk[nb][dep] = sm.qk[cb][t];
+                        ++dep;
+                    }
+                    sm.qcur = nb;
+                    sm.qn = dep;
+                }
+            }
+            __syncthreads();
+            if (MODE == kHullQuick) return HullOut{false, sm.qn, false};
+            // into entries 0..h-1 of the region arrays
+            const int cq = sm.qcur, h = sm.qn;
+            if (L < h) {
+                sm.S[L] = sm.qS[cq][L];
+                if (WT) sm.W[L] = sm.qW[cq][L];
+                sm.idx[L] = (uint16_t)sm.qk[cq][L];
+            }
+            __syncthreads();
+            return HullOut{false, h, false};
+        }
+        if (MODE == kHullQuick) return HullOut{false, 0, true};
+    }
+
+    if constexpr (MODE == kHullQuick) {
+        return HullOut{false, 0, true};
+    } else {
     // ---- thread hull: monotone chain, the region as its stack; pushes come
     // from registers, a pop reloads the entry under the new top
     const int r0 = L * RS;
@@ -358,7 +571,8 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT>& sm, const flo
         }
     }
     __syncthreads();
-    return HullOut{false, sm.cnt[0]};
+    return HullOut{false, sm.cnt[0], false};
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -370,14 +584,14 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
                                                    float sign, float* __restrict__ out,
                                                    int32_t* __restrict__ block_id,
                                                    int32_t* __restrict__ row_flag) {
-    __shared__ HullSmem<NT, P, WT> sm;
+    __shared__ HullSmem<NT, P, WT, kHullBoth> sm;
     const int64_t row = blockIdx.x;
     const float* gy = y + row * n;
     const float* gw = WT ? w + row * n : nullptr;
     const int len = (int)n;
     float yv[P];
     double ps[P], pw[P], s0, w0;
-    const HullOut ho = block_hull<NT, P, WT>(sm, gy, gw, len, sign, yv, ps, pw, s0, w0);
+    const HullOut ho = block_hull<NT, P, WT, kHullBoth>(sm, gy, gw, len, sign, yv, ps, pw, s0, w0);
 
     const int L = threadIdx.x;
     const int base = L * P;
@@ -443,22 +657,25 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
 // ----------------------------------------------------------------------------
 // Long rows, phase 1: one workgroup per chunk builds the chunk's hull and
 // writes it once to its slot (paper section 3.3), with the chunk's totals.
+// The first kernel tries quickhull (and the strictly increasing case) with
+// little LDS and few registers, so that many workgroups share a CU; a chunk it
+// gives up on is marked, and the second kernel redoes only the marked chunks
+// with chains and merges.
 // ----------------------------------------------------------------------------
-template <bool WT>
-__global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict__ y,
-                                                         const float* __restrict__ w, int64_t n,
-                                                         int m, float sign, LongWs ws, int full_slots) {
+template <int MODE, bool WT>
+__device__ __forceinline__ void chunk_hull(const float* __restrict__ y, const float* __restrict__ w,
+                                           int64_t n, int m, float sign, const LongWs& ws,
+                                           int full_slots, HullSmem<kLongNT, kLongP, WT, MODE>& sm,
+                                           int64_t gid /* row * m + chunk */) {
     constexpr int NT = kLongNT, P = kLongP, C = kChunk;
-    __shared__ HullSmem<NT, P, WT> sm;
-    const int64_t gid = blockIdx.x;  // row * m + chunk
     const int64_t row = gid / m;
     const int j = (int)(gid - row * m);
     const int64_t off = row * n + (int64_t)j * C;
     const int len = (int)min((int64_t)C, n - (int64_t)j * C);
     float yv[P];
     double ps[P], pw[P], s0, w0;
-    const HullOut ho = block_hull<NT, P, WT>(sm, y + off, WT ? w + off : nullptr, len, sign, yv, ps,
-                                             pw, s0, w0);
+    const HullOut ho = block_hull<NT, P, WT, MODE>(sm, y + off, WT ? w + off : nullptr, len, sign, yv,
+                                                   ps, pw, s0, w0);
     const int L = threadIdx.x;
     const int base = L * P;
     const int h = ho.h;
@@ -490,6 +707,24 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
             if (e >= 0) wr->v[e] = make_double2(ps[b], WT ? pw[b] : (double)k);
         }
         cflag |= kChunkInc;
+    } else if (MODE == kHullQuick && (ho.all || ho.fail)) {
+        // a full slot for an increasing chunk (it is staged through the
+        // regions), or a hull quickhull gave up on: the second kernel
+        cflag |= kChunkRedo;
+        if (L == 0) atomicAdd(ws.redo_n, 1);
+    } else if constexpr (MODE == kHullQuick) {
+        // the quickhull vertex list
+        const int cq = sm.qcur;
+        for (int i = L; i < h; i += NT) {
+            const int k = min(sm.qk[cq][i], len);
+            const double s = sm.qS[cq][i];
+            const double wv = sm.qW[cq][i];
+            ws.slot_idx[slot + i] = (uint16_t)k;
+            ws.slot_S[slot + i] = s;
+            if (WT) ws.slot_W[slot + i] = wv;
+            const int e = wslot(i);
+            if (e >= 0) wr->v[e] = make_double2(s, wv);
+        }
     } else if (ho.all) {
         // every point 0..len is a vertex: stage the points' S (and W) in LDS
         // (point k at k + (k-1)/P, so that threads writing their own points hit
@@ -533,6 +768,29 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_hulls(const float* __restrict
     }
 }
 
+template <bool WT>
+__global__ __launch_bounds__(kLongNT, WT ? 3 : 4) void k_chunk_hulls(const float* __restrict__ y,
+                                                         const float* __restrict__ w, int64_t n,
+                                                         int m, float sign, LongWs ws, int full_slots) {
+    __shared__ HullSmem<kLongNT, kLongP, WT, kHullQuick> sm;
+    chunk_hull<kHullQuick, WT>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x);
+}
+
+// A fixed grid that walks the chunks and redoes the marked ones.
+template <bool WT>
+__global__ __launch_bounds__(kLongNT) void k_chunk_redo(const float* __restrict__ y,
+                                                        const float* __restrict__ w, int64_t n,
+                                                        int m, float sign, LongWs ws, int full_slots,
+                                                        int64_t nchunks) {
+    __shared__ HullSmem<kLongNT, kLongP, WT, kHullChains> sm;
+    if (*ws.redo_n == 0) return;  // nothing marked (a fresh workspace scans anyway)
+    for (int64_t gid = blockIdx.x; gid < nchunks; gid += gridDim.x) {
+        if (!(ws.chunk_flag[gid] & kChunkRedo)) continue;
+        chunk_hull<kHullChains, WT>(y, w, n, m, sign, ws, full_slots, sm, gid);
+        __syncthreads();
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Long rows, phase 3: every element takes the slope of the row-hull edge above
 // it (paper equation (3), section 3.4).
@@ -571,6 +829,7 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
             }
         }
     };
+    if (gid == 0 && tid == 0) *ws.redo_n = 0;  // for the next call's chunk kernels
     if (ws.row_flag[row] & kFlagNonfinite) {
         const float nan = __builtin_nanf("");
         for (int g = 0; g < G; ++g) {
@@ -714,6 +973,15 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
     else
         hipLaunchKernelGGL(k_chunk_hulls<false>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
                            sh.sign, ws, full_slots);
+    timed_end(st);
+    timed_begin(kPhaseChunkRedo, st);
+    const unsigned nredo = nblk < kRedoGrid ? nblk : (unsigned)kRedoGrid;
+    if (wt)
+        hipLaunchKernelGGL(k_chunk_redo<true>, dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+                           sh.sign, ws, full_slots, (int64_t)nblk);
+    else
+        hipLaunchKernelGGL(k_chunk_redo<false>, dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+                           sh.sign, ws, full_slots, (int64_t)nblk);
     timed_end(st);
     bool rec_done = true;
     hipError_t e = copy_control ? launch_copy_merge(sh, ws, st) : launch_segment_merge(sh, ws, st, &rec_done);

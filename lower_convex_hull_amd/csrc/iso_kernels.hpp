@@ -15,6 +15,9 @@ constexpr int kLongNT = 256;
 constexpr int kLongP = 16;
 constexpr int kChunk = kLongNT * kLongP;  // 4096
 constexpr int kShortMax = 4096;
+constexpr int kQhMax = 64;          // vertices of a block hull built by quickhull
+constexpr int kQhLevels = 10;       // quickhull levels before the chains-and-merges fallback
+constexpr int kRedoGrid = 768;      // workgroups of the fallback chunk kernel (3 per CU)
 constexpr int kMergeNT = 1024;
 constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
 constexpr int kWinK = 16;           // hull vertices kept at each end of a chunk's window
@@ -36,6 +39,8 @@ constexpr int kFlagData = kFlagNonfinite | kFlagWeight;
 // hull vertex (position = point index) and the chunk's slot is not written;
 // its points are recomputed from the input and the per-thread checkpoints.
 constexpr int kChunkInc = 4;
+// Chunk flag: the first chunk kernel left this chunk to the second.
+constexpr int kChunkRedo = 8;
 
 // Reconstruction record of one chunk, written by the merge phase.
 //   lo < 0: no vertex of the row's hull lies in the chunk; every element of
@@ -100,6 +105,7 @@ struct LongWs {
     double2* cst;         // [R*m] chunk starts relative to their group's start
     int32_t* gpre;        // [R*m] vertices before each segment of a group's list
     int32_t* root_n;      // [R] segments in the root list (desc_scr) of each row
+    int32_t* redo_n;      // [1] chunks the first chunk kernel left over (reset by the expansion)
     double* ck_S;         // [R*m*(kLongNT+1)] S at each thread's first point (and the chunk end)
     double* ck_W;         // (weighted only)
     // the call's inputs, for points recomputed from them
@@ -131,7 +137,7 @@ struct LongShape {
 
 // Phases of the launch timing (the ISO_PHASE_* values of iso.h).
 constexpr int kPhaseShort = 0, kPhaseChunk = 1, kPhaseMerge = 2, kPhaseExpand = 3,
-              kPhaseCopyBridge = 4, kPhaseCopyMove = 5, kPhaseMergeTop = 6;
+              kPhaseCopyBridge = 4, kPhaseCopyMove = 5, kPhaseMergeTop = 6, kPhaseChunkRedo = 7;
 
 // Launch timing for benchmarks (iso_timing_enable / iso_timing_read): when
 // enabled, timed_begin records an event before a launch and timed_end one

@@ -30,7 +30,7 @@ ISO_F_COPY_CONTROL = 4
 ISO_F_WEIGHTED_HINT = 0x100
 
 ISO_PHASE_NAMES = ("short_rows", "chunk_hulls", "merge", "expand", "copy_bridge", "copy_move",
-                   "merge_top")
+                   "merge_top", "chunk_redo")
 
 EXPORTS = ("iso_fit", "iso_fit_ex", "iso_workspace_bytes", "iso_status_str", "iso_release",
            "iso_chunk_size", "iso_short_row_max", "iso_timing_enable", "iso_timing_read")
