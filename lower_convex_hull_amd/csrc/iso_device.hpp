@@ -644,13 +644,31 @@ __device__ __forceinline__ void team_move(const Arr& ar, int l0, int A, int r0, 
 // Lemma 4.2 stops at the one pair (A, B) whose line has A's neighbours in L
 // and B's neighbours in R on or above it, A's left neighbour and B's right one
 // strictly above (the outermost of collinear vertices).  These four local
-// conditions single that pair out, so the wave tests the 16 x 16 pairs
-// nearest the shared point at once, four per lane, and walks only when the
-// test does not find exactly one pair.  Every lane of the wave calls it.
+// conditions single that pair out, so the wave tests the 8 x 8 pairs nearest
+// the shared point at once (one per lane), then the 16 x 16 nearest (four per
+// lane), and walks only when neither finds exactly one pair.  Every lane of
+// the wave calls it.
 __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r0, int cR, int lane) {
     {
         const Pt PA = ar.pt(l0 + cL - 2), Ps = ar.pt(r0), PB = ar.pt(r0 + 1);
         if (cross3(PA, Ps, PB) > 0.0) return make_int2(cL - 1, 1);  // convex at the shared point
+    }
+    {
+        // first the 8 x 8 pairs nearest the shared point, one per lane
+        const int a = cL - 2 - (lane & 7), b = 1 + (lane >> 3);
+        bool hit = false;
+        if (a >= 0 && b <= cR - 1) {
+            const Pt La = ar.pt(l0 + a), Ln = ar.pt(l0 + a + 1), Rb = ar.pt(r0 + b), Rp = ar.pt(r0 + b - 1);
+            const Pt Lp = a > 0 ? ar.pt(l0 + a - 1) : La;
+            const Pt Rn = b < cR - 1 ? ar.pt(r0 + b + 1) : Rb;
+            hit = (a == 0 || cross3(Lp, La, Rb) > 0.0) && (b == cR - 1 || cross3(La, Rb, Rn) > 0.0) &&
+                  cross3(La, Ln, Rb) <= 0.0 && cross3(La, Rp, Rb) <= 0.0;
+        }
+        const uint64_t bal = __ballot(hit);
+        if (__popcll(bal) == 1) {
+            const int f = __ffsll((long long)bal) - 1;
+            return make_int2(cL - 2 - (f & 7), 1 + (f >> 3));
+        }
     }
     const int i = lane & 15, b0 = 1 + 4 * (lane >> 4);
     const int a = cL - 2 - i;

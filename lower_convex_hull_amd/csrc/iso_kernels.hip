@@ -63,12 +63,15 @@ struct HullSmem {
     int ired[NT / 64 + 1];
     double end_s, end_w;          // S and W of point len (padding points repeat it)
     int flag;
-    // quickhull: the vertex list (two buffers), and per chord the key of the
-    // farthest point below it and that point's coordinates
+    // quickhull: every point's S (and W) at k + (k-1)/P (the region arrays
+    // serve where they exist), the vertex list (two buffers), and per chord
+    // the key of the farthest point below it
+    static constexpr int NP = MODE == kHullQuick ? NT * RS : 1;
+    double pS[NP];
+    double pW[WT ? NP : 1];
     int32_t qk[2][NQ];
     double qS[2][NQ], qW[2][NQ];
     unsigned long long qkey[NQ];
-    double qnS[NQ], qnW[NQ];
     int qn, qcur, qstate;
 };
 
@@ -248,6 +251,21 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     // a few levels with few vertices; a block that needs more levels or more
     // vertices falls back to the chains and merges below.
     if constexpr (MODE != kHullChains) {
+        double* pS = MODE == kHullQuick ? sm.pS : sm.S;
+        double* pW = MODE == kHullQuick ? sm.pW : sm.W;
+        auto sk = [](int k) { return k + (k - 1) / P; };  // k >= 1
+        // the key of a candidate: the positive f64 depth measure with its low
+        // 13 bits giving way to the index, so that the largest key is the
+        // farthest point and, on a tie, the lowest index
+        auto mkkey = [](double c, int k) {
+            return ((unsigned long long)__double_as_longlong(c) & ~0x1fffull) |
+                   (unsigned long long)(0x1fff - k);
+        };
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            pS[sk(base + b + 1)] = ps[b];
+            if (WT) pW[sk(base + b + 1)] = pw[b];
+        }
         uint32_t alive = 0;
 #pragma unroll
         for (int b = 0; b < P; ++b)
@@ -268,31 +286,30 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
         for (int lv = 0; lv < kQhLevels; ++lv) {
             const int cb = sm.qcur, nv = sm.qn;
             const int32_t* vk = sm.qk[cb];
-            // the chord over this thread's first point: vk[i0] <= base < vk[i0+1]
-            int i0 = 0;
-            if (alive) {
-                int hi = nv - 1;
-                while (hi - i0 > 1) {
-                    const int mid = (i0 + hi) >> 1;
-                    if (vk[mid] <= base) i0 = mid;
-                    else hi = mid;
-                }
-            }
-            int qi = 0;                 // this thread's last chord
+            int qi = 0;                       // this thread's last chord
             unsigned long long qbest = 0ull;  // and its best key there
             if (alive) {
-                // chord i runs from vertex vk[i] to vertex nk = vk[i+1]; reloaded
-                // only when this thread's points pass a vertex
-                int i = i0, nk = vk[i0 + 1];
-                Pt A{sm.qW[cb][i0], sm.qS[cb][i0]}, B{sm.qW[cb][i0 + 1], sm.qS[cb][i0 + 1]};
-                unsigned long long best = 0ull;
-#pragma unroll
-                for (int b = 0; b < P; ++b) {
-                    if (!((alive >> b) & 1u)) continue;
+                // the chord over this thread's first point: vk[i] <= base < vk[i+1]
+                int i = 0, hi = nv - 1;
+                while (hi - i > 1) {
+                    const int mid = (i + hi) >> 1;
+                    if (vk[mid] <= base) i = mid;
+                    else hi = mid;
+                }
+                // chord i runs from vertex vk[i] to vertex nk; reloaded only
+                // when this thread's points pass a vertex (a point that became
+                // a vertex lies on its chords and drops out)
+                int nk = vk[i + 1];
+                Pt A{sm.qW[cb][i], sm.qS[cb][i]}, B{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
+                double bc = 0.0;
+                int bk = 0;
+                for (uint32_t mm = alive; mm; mm &= mm - 1u) {
+                    const int b = lsb32(mm);
                     const int k = base + b + 1;
                     if (k >= nk) {
-                        if (best) atomicMax(&sm.qkey[i], best);
-                        best = 0ull;
+                        if (bk) atomicMax(&sm.qkey[i], mkkey(bc, bk));
+                        bc = 0.0;
+                        bk = 0;
                         do {
                             ++i;
                             nk = vk[i + 1];
@@ -300,21 +317,19 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                         A = Pt{sm.qW[cb][i], sm.qS[cb][i]};
                         B = Pt{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
                     }
-                    const Pt Pk{WT ? pw[b] : (double)k, ps[b]};
+                    const Pt Pk{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
                     const double c = cross3(A, Pk, B);
                     if (c > 0.0) {
-                        // the farthest point below the chord, the lowest index on a tie
-                        // (the low 13 bits of the positive f64 give way to the index)
-                        const unsigned long long key =
-                            ((unsigned long long)__double_as_longlong(c) & ~0x1fffull) |
-                            (unsigned long long)(0x1fff - k);
-                        best = key > best ? key : best;
+                        if (c > bc) {
+                            bc = c;
+                            bk = k;
+                        }
                     } else {
                         alive &= ~(1u << b);
                     }
                 }
                 qi = i;
-                qbest = best;
+                qbest = bk ? mkkey(bc, bk) : 0ull;
             }
             {
                 // one atomic per wave when all of its threads with a candidate
@@ -338,31 +353,9 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 }
             }
             __syncthreads();
-            // the winners write their coordinates for the new vertex list
-            if (alive) {
-                int i = i0, nk = vk[i0 + 1];
-                int win = (int)(0x1fff - (sm.qkey[i0] & 0x1fffull));
-#pragma unroll
-                for (int b = 0; b < P; ++b) {
-                    if (!((alive >> b) & 1u)) continue;
-                    const int k = base + b + 1;
-                    if (k >= nk) {
-                        do {
-                            ++i;
-                            nk = vk[i + 1];
-                        } while (nk <= k);
-                        win = (int)(0x1fff - (sm.qkey[i] & 0x1fffull));
-                    }
-                    if (win == k) {
-                        sm.qnS[i] = ps[b];
-                        sm.qnW[i] = WT ? pw[b] : (double)k;
-                        alive &= ~(1u << b);
-                    }
-                }
-            }
-            __syncthreads();
             if (L < 64) {
-                // one wave inserts the new vertices after their chords' starts
+                // one wave inserts each chord's farthest point after the
+                // chord's start, its coordinates from the staged points
                 const bool found = L < nv - 1 && sm.qkey[L] != 0ull;
                 const uint64_t bal = __ballot(found);
                 const int pre = __popcll(bal & ((1ull << L) - 1ull));
@@ -373,9 +366,10 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                     sm.qS[nb][L + pre] = sm.qS[cb][L];
                     sm.qW[nb][L + pre] = sm.qW[cb][L];
                     if (found) {
-                        sm.qk[nb][L + pre + 1] = (int)(0x1fff - (sm.qkey[L] & 0x1fffull));
-                        sm.qS[nb][L + pre + 1] = sm.qnS[L];
-                        sm.qW[nb][L + pre + 1] = sm.qnW[L];
+                        const int k = (int)(0x1fff - (sm.qkey[L] & 0x1fffull));
+                        sm.qk[nb][L + pre + 1] = k;
+                        sm.qS[nb][L + pre + 1] = pS[sk(k)];
+                        sm.qW[nb][L + pre + 1] = WT ? pW[sk(k)] : (double)k;
                     }
                 }
                 if (L < kQhMax) sm.qkey[L] = 0ull;

@@ -69,13 +69,14 @@ struct WinRec {
 };
 
 // The same for the hull of a group of kGroup chunks (first merge stage): its
-// vertex count, the number of segments in its list, the (S, W) of its first
+// vertex count, the number of segments in its list, its data flags, the (S, W) of its first
 // and last kGWinK vertices relative to the group's first point, and for each
 // of those the chunk and the position in that chunk's hull (packed by mktag).
 struct GroupWin {
     int32_t h;
     int32_t nseg;
-    int32_t pad[2];
+    int32_t flags;  // the group's data flags (kFlagData bits of its chunks)
+    int32_t pad;
     double2 v[2 * kGWinK];
     int32_t tag[2 * kGWinK];
 };

@@ -466,6 +466,13 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         gwo->h = hg;
         gwo->nseg = nseg;
     }
+    if (wid == 0) {
+        // the group's data flags, for the second stage
+        int f = wlane < gc ? (ws.chunk_flag[rb + j0 + wlane] & kFlagData) : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) f |= __shfl_xor(f, d);
+        if (wlane == 0) gwo->flags = f;
+    }
     if (ng == 1) {
         // the group is the whole row: its list is the root
         if (tid == 0) sflag = 0;
@@ -503,14 +510,14 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     const int tid = threadIdx.x;
 
     // group hull counts; the fast path needs every group hull whole in its window
-    int hgv = 0;
-    if (tid < ng) hgv = ws.gwin[gb + tid].h;
+    int hgv = 0, f = 0;
+    if (tid == 0) sflag = 0;
+    if (tid < ng) {
+        hgv = ws.gwin[gb + tid].h;
+        f = ws.gwin[gb + tid].flags;
+    }
     const bool fast = (__syncthreads_and(tid >= ng || hgv <= E) != 0) && ng <= kTopFastMax &&
                       m < kTagMaxChunks;
-    if (tid == 0) sflag = 0;
-    __syncthreads();
-    int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
     if (f) atomicOr(&sflag, f);
 
     // group starts (exclusive scan of the group totals)
@@ -541,14 +548,15 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         const Arr ar{aS, aS + ng * E, reinterpret_cast<int32_t*>(aS + 2 * ng * E)};
         int32_t* CNT = ar.tag + ng * E;
         for (int t = tid; t < ng * E; t += NT) {
+            // every window entry is read (unused ones too), so the loads do not
+            // wait for the group's vertex count
             const int g = t / E, e = t - g * E;
             const GroupWin* gw = ws.gwin + gb + g;
-            if (e < gw->h) {
-                const double2 v = gw->v[e];
-                ar.S[t] = gS[g] + v.x;
-                ar.W[t] = gW[g] + v.y;
-                ar.tag[t] = gw->tag[e];
-            }
+            const double2 v = gw->v[e];
+            const int tg = gw->tag[e];
+            ar.S[t] = gS[g] + v.x;
+            ar.W[t] = gW[g] + v.y;
+            ar.tag[t] = tg;
         }
         for (int g = tid; g < ng; g += NT) CNT[g] = ws.gwin[gb + g].h;
         __syncthreads();
@@ -623,8 +631,10 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         };
         for (int t = tid; t < nr2; t += NT) {
             const int4 d = D[t];
-            s_ilo[t] = seg_of(d.x, d.y);
-            s_ihi[t] = seg_of(d.x, d.z);
+            // a whole group list (always so where every merge was convex)
+            // needs no search
+            s_ilo[t] = d.y == 0 ? 0 : seg_of(d.x, d.y);
+            s_ihi[t] = d.z == GH[d.x] - 1 ? GW[d.x].nseg - 1 : seg_of(d.x, d.z);
         }
         __syncthreads();
         if (tid == 0) {

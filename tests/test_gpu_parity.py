@@ -307,6 +307,24 @@ def test_nonfinite_rows_and_bad_weights(torch):
         assert st == iso.ISO_ERR_WEIGHT
 
 
+def test_nonfinite_and_bad_weight_in_a_later_group(torch):
+    """Rows long enough for two merge stages: a data flag raised in a chunk of a
+    later group reaches the row's status through the group records."""
+    n = 300_000  # 74 chunks, two groups
+    y, _ = inputs.noisy(2, n, 15)
+    y[1, 280_000] = np.nan
+    st, out, bid = gpu_fit(torch, y)
+    assert st == iso.ISO_WARN_NONFINITE
+    assert np.all(np.isnan(out[1])) and np.all(bid[1] == -1) and not np.isnan(out[0]).any()
+    _, z64, _ = oracle.fit_rows_f32(y[[0]])
+    assert fitcheck.parity(y[[0]], None, out[[0]], z64)[0]
+    y2, _ = inputs.noisy(2, n, 16)
+    w = np.ones_like(y2)
+    w[1, 290_000] = 0.0
+    st, _, _ = gpu_fit(torch, y2, w)
+    assert st == iso.ISO_ERR_WEIGHT
+
+
 def test_deterministic(torch):
     y, _ = inputs.noisy(1, 300_000, 15)
     _, a, ba = gpu_fit(torch, y)
