@@ -424,8 +424,22 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         __syncthreads();
         const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, Wn, HC, lS, lW, WT,
                         inc_src(ws, row, m, j0)};
-        for (int span = 1; span < gc; span <<= 1)
-            merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
+        // when the chain of chunk hulls turns strictly left at every junction
+        // it is convex, so the group hull is the concatenation (each later
+        // hull without its first point, the shared one)
+        bool jc = true;
+        if (tid + 1 < gc) {
+            const int h = HC[tid];
+            jc = cross3(X.vtx(tid, h - 2, tid + 1), X.vtx(tid + 1, 0, tid + 1), X.vtx(tid + 1, 1, tid + 1)) > 0.0;
+        }
+        if (__syncthreads_and(jc)) {
+            for (int i = tid; i < gc; i += NT) D[i] = mkdesc(i, i == 0 ? 0 : 1, HC[i] - 1);
+            if (tid == 0) CNT[0] = gc;
+            __syncthreads();
+        } else {
+            for (int span = 1; span < gc; span <<= 1)
+                merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
+        }
         nseg = CNT[0];
         if (wid == 0) {
             int v = 0;
@@ -612,8 +626,21 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
                          ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
                          inc_src(ws, row, m, 0)};
         const GroupView X{GW, GH, gS, gW, ws.desc + rb, ws.gpre + rb, ws.cst + rb, Cv, WT};
-        for (int span = 1; span < ng; span <<= 1)
-            merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
+        // a chain of group hulls turning strictly left at every junction is
+        // the row hull: the concatenation
+        bool jc = true;
+        if (tid + 1 < ng) {
+            const int h = GH[tid];
+            jc = cross3(X.vtx(tid, h - 2, tid + 1), X.vtx(tid + 1, 0, tid + 1), X.vtx(tid + 1, 1, tid + 1)) > 0.0;
+        }
+        if (__syncthreads_and(jc)) {
+            for (int g = tid; g < ng; g += NT) D[g] = make_int4(g, g == 0 ? 0 : 1, GH[g] - 1, 0);
+            if (tid == 0) CNT[0] = ng;
+            __syncthreads();
+        } else {
+            for (int span = 1; span < ng; span <<= 1)
+                merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
+        }
 
         // the root list over groups, expanded into segments of chunk hulls:
         // first the range of group-list segments each root entry covers, then
