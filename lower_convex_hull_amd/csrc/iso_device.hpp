@@ -619,6 +619,28 @@ __device__ __forceinline__ void team_move(const Arr& ar, int l0, int A, int r0, 
                                           int T, bool act) {
     const int n = act ? cR - B : 0;
     const int dst = l0 + A + 1, src = r0 + B;
+    if (T == 64) {
+        // one merge per wave: n is the same on every lane
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + x;
+            const bool a = i < n;
+            double s = 0.0, w = 0.0;
+            int t = 0;
+            if (a) {
+                s = ar.S[src + i];
+                w = ar.W[src + i];
+                t = ar.tag[src + i];
+            }
+            wave_sync();
+            if (a) {
+                ar.S[dst + i] = s;
+                ar.W[dst + i] = w;
+                ar.tag[dst + i] = t;
+            }
+            wave_sync();
+        }
+        return;
+    }
     for (int i0 = 0;; i0 += T) {
         const int i = i0 + x;
         const bool a = i < n;
@@ -724,34 +746,41 @@ __device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn
 // Prefix counts over a row's root list D of nroot segments (at most one per
 // chunk, in chunk order) for the reconstruction: vb[i] = root vertices before
 // segment i (block ids), and fs[j] = segments in chunks before chunk j, which
-// is the index of the first segment whose chunk is >= j.
+// is the index of the first segment whose chunk is >= j.  rc (LDS, nroot
+// ints) receives the segments' chunks so that fs is a binary search; vb0, when
+// given, already holds vb (the compact-array path knows it).
 template <int NT>
 __device__ __forceinline__ void root_prefixes(const uint2* D, int nroot, int m, int32_t* vb, int32_t* fs,
-                                              int* ired) {
+                                              int* ired, int32_t* rc, const int32_t* vb0) {
     const int tid = threadIdx.x;
-    for (int j = tid; j < m; j += NT) fs[j] = 0;
-    __syncthreads();
-    for (int i = tid; i < nroot; i += NT) fs[dchunk(D[i])] = 1;
-    __syncthreads();
-    int carry = 0, vcarry = 0;
-    const int top = max(m, nroot);
-    for (int t0 = 0; t0 < top; t0 += NT) {
-        const int j = t0 + tid;
-        int tot;
-        const int f = j < m ? fs[j] : 0;
-        const int xj = wg_excl_scan_int<NT>(f, ired, &tot);
-        if (j < m) fs[j] = carry + xj;
-        carry += tot;
+    int carry = 0;
+    for (int t0 = 0; t0 < nroot; t0 += NT) {
+        const int i = t0 + tid;
         int v = 0;
-        if (j < nroot) {
-            const uint2 d = D[j];
+        if (i < nroot) {
+            const uint2 d = D[i];
+            rc[i] = dchunk(d);
             v = dhi(d) - dlo(d) + 1;
         }
+        if (vb0) {
+            if (i < nroot) vb[i] = vb0[i];
+            continue;
+        }
+        int tot;
         const int xv = wg_excl_scan_int<NT>(v, ired, &tot);
-        if (j < nroot) vb[j] = vcarry + xv;
-        vcarry += tot;
+        if (i < nroot) vb[i] = carry + xv;
+        carry += tot;
     }
     __syncthreads();
+    for (int j = tid; j < m; j += NT) {
+        int lo = 0, hi = nroot;  // first segment whose chunk is >= j
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (rc[mid] < j) lo = mid + 1;
+            else hi = mid;
+        }
+        fs[j] = lo;
+    }
 }
 
 // The reconstruction record of chunk j (Corollary 4.5) from the root list and

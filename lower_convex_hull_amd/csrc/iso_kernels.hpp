@@ -25,8 +25,8 @@ constexpr int kGWinK = 32;          // the same for a group hull's window
 constexpr int kGroup = 64;          // chunks per group of the first merge stage
 constexpr int kGroupNT = 1024;
 constexpr int kTopNT = 1024;
-constexpr int kTopMax = 96;         // groups per row the second stage keeps in LDS
-constexpr int kTopFastMax = 96;     // groups per row for the second stage's compact-array path
+constexpr int kTopMax = 72;         // groups per row the second stage keeps in LDS
+constexpr int kTopFastMax = 72;     // groups per row for the second stage's compact-array path
 constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed to a wave
 constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
 constexpr int kHardCap = 256;     // merges per level a wave may take over

@@ -501,13 +501,26 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             ws.st_S[rb + j] = lS[j];
             if (WT) ws.st_W[rb + j] = lW[j];
         }
-        root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired);
+        root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired, slast, nullptr);
         if (tid == 0) {
             ws.row_flag[row] = sflag;
             ws.root_n[row] = nseg;
         }
     }
 }
+
+// Dynamic LDS of the second stage: group starts gS, gW (8 B each), then
+// either the segment-list path's D, SCR (16 B each), GW, MI (8 B per merge),
+// CNT, GH (4 B each), or the compact-array path's 2 kGWinK entries per group
+// (S, W, tag) and CNT; after that the root segments' chunks and their vertex
+// prefix (at most one segment per chunk and one per window entry).
+__host__ __device__ inline size_t top_lds_main(int ng) {
+    const size_t gen = (size_t)ng * (32 + sizeof(GroupWin) + 8) + (size_t)(ng / 2 + 1) * 8;
+    const size_t fast = (size_t)ng * (2 * kGWinK) * 20 + (size_t)ng * 4;
+    return (size_t)ng * 16 + (gen > fast ? gen : fast);
+}
+__host__ __device__ inline int top_root_cap(int ng, int m) { return m < ng * 2 * kGWinK ? m : ng * 2 * kGWinK; }
+inline size_t top_lds_bytes(int ng, int m) { return top_lds_main(ng) + (size_t)top_root_cap(ng, m) * 8; }
 
 template <bool WT>
 __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
@@ -555,6 +568,9 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     }
     __syncthreads();
     uint2* R = ws.desc_scr + rb;  // the root list, as segments of chunk hulls
+    // after both paths' LDS: the root segments' chunks (and, on the compact
+    // path, their vertex prefix), for the record prefix counts
+    int32_t* rcbuf = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(top_lds) + top_lds_main(ng));
     int nroot;
     if (fast) {
         // ---- every group hull is short: merge compact arrays in LDS
@@ -577,6 +593,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         merge_arrays<NT>(ar, CNT, ng, E);
         const int hr = CNT[0];
         // one root segment per run of a chunk's vertices
+        int32_t* vbl = rcbuf + top_root_cap(ng, m);  // after the chunk-id buffer
         uint16_t* R16 = reinterpret_cast<uint16_t*>(R);
         uint32_t* R32 = reinterpret_cast<uint32_t*>(R);
         int carry = 0;
@@ -595,6 +612,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             if (st) {
                 R32[2 * sidx] = (uint32_t)c;
                 R16[4 * sidx + 2] = (uint16_t)tpos(ar.tag[t]);
+                vbl[sidx] = t;  // root vertices before the segment
             }
             if (en) R16[4 * sidx + 3] = (uint16_t)tpos(ar.tag[t]);
             carry += tot;
@@ -660,7 +678,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             const int4 d = D[t];
             // a whole group list (always so where every merge was convex)
             // needs no search
-            s_ilo[t] = d.y == 0 ? 0 : seg_of(d.x, d.y);
+            s_ilo[t] = d.y == 0 ? 0 : (d.y == 1 ? (ws.gpre[rb + d.x * G + 1] > 1 ? 0 : 1) : seg_of(d.x, d.y));
             s_ihi[t] = d.z == GH[d.x] - 1 ? GW[d.x].nseg - 1 : seg_of(d.x, d.z);
         }
         __syncthreads();
@@ -699,20 +717,12 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     }
     __syncthreads();
     // prefix counts of the root list for the expansion's records
-    root_prefixes<NT>(R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ired);
+    root_prefixes<NT>(R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ired, rcbuf,
+                      fast ? rcbuf + top_root_cap(ng, m) : nullptr);
     if (tid == 0) {
         ws.row_flag[row] = sflag;
         ws.root_n[row] = nroot;
     }
-}
-
-size_t top_lds_bytes(int ng) {
-    // group starts gS, gW (8 B each), then either the segment-list path's D,
-    // SCR (16 B each), GW, MI (8 B per merge), CNT, GH (4 B each), or the
-    // compact-array path's 2 kWinK entries per group (S, W, tag) and CNT
-    const size_t gen = (size_t)ng * (32 + sizeof(GroupWin) + 8) + (size_t)(ng / 2 + 1) * 8;
-    const size_t fast = (size_t)ng * (2 * kGWinK) * 20 + (size_t)ng * 4;
-    return (size_t)ng * 16 + (gen > fast ? gen : fast);
 }
 
 }  // namespace
@@ -741,10 +751,10 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
                                ng, ws);
         timed_end(st);
         if (ng > 1) {
-            const size_t lds = top_lds_bytes(ng);
+            const size_t lds = top_lds_bytes(ng, sh.m);
             static bool attr_set = false;
             if (!attr_set) {
-                const int maxb = (int)top_lds_bytes(kTopMax);
+                const int maxb = (int)top_lds_bytes(kTopMax, kTopMax * kGroup);
                 (void)hipFuncSetAttribute((const void*)k_top_merge<true>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
                 (void)hipFuncSetAttribute((const void*)k_top_merge<false>,
