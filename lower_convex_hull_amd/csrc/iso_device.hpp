@@ -783,42 +783,46 @@ __device__ __forceinline__ void root_prefixes(const uint2* D, int nroot, int m, 
     }
 }
 
+// Bit of a row's root-segment count meaning that the merge stored the slope of
+// the root edge into every root segment (rslope).
+constexpr int kRootSlopes = 1 << 30;
+
 // The reconstruction record of chunk j (Corollary 4.5) from the root list and
 // its prefix counts: the range of the chunk's surviving hull vertices and the
-// slopes of the edges into and out of it, or the one edge it lies under.
-__device__ __forceinline__ ChunkRec chunk_record(const RowView X, const uint2* D, int nroot,
-                                                 const int32_t* vb, const int32_t* fs, int j) {
+// slopes of the edges into and out of it, or the one edge it lies under.  The
+// edge slopes come from rslope when the merge stored them, else from the
+// vertices (X).
+template <class V>
+__device__ __forceinline__ ChunkRec chunk_record(const V X, const uint2* D, int nroot_bits,
+                                                 const int32_t* vb, const int32_t* fs,
+                                                 const double* rslope, int j) {
+    const bool have = (nroot_bits & kRootSlopes) != 0;
+    const int nroot = nroot_bits & ~kRootSlopes;
     const int i = fs[j];  // first root segment with chunk >= j
-    const uint2 d = D[min(i, nroot - 1)];
+    const int ic = min(i, nroot - 1);
+    const uint2 d = D[ic];
     ChunkRec rc;
     rc.pad = 0;
+    rc.vb = vb[ic];
+    auto slope_into = [&](int s) {  // the root edge into segment s >= 1
+        if (have) return rslope[s];
+        const uint2 p = D[s - 1], q = D[s];
+        const Pt A = X.vtx(dchunk(p), dhi(p), j), B = X.vtx(dchunk(q), dlo(q), j);
+        return (B.s - A.s) / (B.w - A.w);
+    };
     if (i < nroot && dchunk(d) == j) {
-        rc.vb = vb[i];
         rc.lo = dlo(d);
         rc.hi = dhi(d);
-        rc.slope_in = 0.0;
-        rc.slope_out = 0.0;
-        if (i > 0) {
-            const uint2 p = D[i - 1];
-            const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(j, dlo(d), j);
-            rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
-        }
-        if (i + 1 < nroot) {
-            const uint2 q = D[i + 1];
-            const Pt A = X.vtx(j, dhi(d), j), Bv = X.vtx(dchunk(q), dlo(q), j);
-            rc.slope_out = (Bv.s - A.s) / (Bv.w - A.w);
-        }
+        rc.slope_in = i > 0 ? slope_into(i) : 0.0;
+        rc.slope_out = i + 1 < nroot ? slope_into(i + 1) : 0.0;
     } else {
         // the chunk lies under one edge, from the last vertex of the previous
         // segment to the first vertex of the next (chunk 0 always holds the
         // row's first point, so i >= 1; the last chunk holds its last point,
         // so i < nroot)
-        const uint2 p = D[i - 1];
-        const Pt A = X.vtx(dchunk(p), dhi(p), j), Bv = X.vtx(dchunk(d), dlo(d), j);
-        rc.vb = vb[i];
         rc.lo = -1;
         rc.hi = -1;
-        rc.slope_in = (Bv.s - A.s) / (Bv.w - A.w);
+        rc.slope_in = slope_into(i);
         rc.slope_out = rc.slope_in;
     }
     return rc;

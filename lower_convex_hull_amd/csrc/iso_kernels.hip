@@ -795,8 +795,8 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
                                                     int32_t* __restrict__ block_id, int rec_done) {
     constexpr int NT = kLongNT, C = kChunk;
     constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
-    __shared__ int vidx[C + 1];
-    __shared__ float vslope[C + 1];
+    __shared__ int vidx[kExpTile + 1];
+    __shared__ float vslope[kExpTile + 1];
     __shared__ ChunkRec s_rc;
     __shared__ int s_inc;
     const int64_t gid = blockIdx.x;
@@ -842,7 +842,8 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
             const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
                             ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
                             inc_src(ws, row, m, 0)};
-            s_rc = chunk_record(X, ws.desc_scr + rb, ws.root_n[row], ws.vb + rb, ws.node_cnt + rb, j);
+            s_rc = chunk_record(X, ws.desc_scr + rb, ws.root_n[row], ws.vb + rb, ws.node_cnt + rb,
+                                ws.rslope + rb, j);
         }
         s_inc = (ws.chunk_flag[gid] & kChunkInc) != 0;
     }
@@ -890,36 +891,69 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         return;
     }
     const size_t slot = (size_t)gid * (C + 1) + rc.lo;
-    for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
-    for (int v = tid; v + 1 < nv; v += NT) {
-        double ds = ws.slot_S[slot + v + 1] - ws.slot_S[slot + v];
-        double dw = WT ? ws.slot_W[slot + v + 1] - ws.slot_W[slot + v]
-                       : (double)((int)ws.slot_idx[slot + v + 1] - (int)ws.slot_idx[slot + v]);
-        vslope[v] = sign * (float)(ds / dw);
-    }
-    __syncthreads();
     const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
-    for (int g = 0; g < G; ++g) {
-        const int e0 = 4 * (g * NT + tid);
-        if (e0 >= len) break;
-        // q = number of the chunk's surviving vertices at or before e0
-        int lo = 0, hi = nv;
-        while (lo < hi) {
-            int mid = (lo + hi) >> 1;
-            if (vidx[mid] <= e0) lo = mid + 1;
-            else hi = mid;
-        }
-        int q = lo;
-        float vv[4];
-        int bb[4];
+    // the slope of edge (v, v+1) of the surviving vertices, from the slot
+    auto edge_slope = [&](int v) {
+        const double ds = ws.slot_S[slot + v + 1] - ws.slot_S[slot + v];
+        const double dw = WT ? ws.slot_W[slot + v + 1] - ws.slot_W[slot + v]
+                             : (double)((int)ws.slot_idx[slot + v + 1] - (int)ws.slot_idx[slot + v]);
+        return sign * (float)(ds / dw);
+    };
+    if (nv <= kExpTile) {
+        for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
+        for (int v = tid; v + 1 < nv; v += NT) vslope[v] = edge_slope(v);
+        __syncthreads();
+        for (int g = 0; g < G; ++g) {
+            const int e0 = 4 * (g * NT + tid);
+            if (e0 >= len) break;
+            // q = number of the chunk's surviving vertices at or before e0
+            int lo = 0, hi = nv;
+            while (lo < hi) {
+                int mid = (lo + hi) >> 1;
+                if (vidx[mid] <= e0) lo = mid + 1;
+                else hi = mid;
+            }
+            int q = lo;
+            float vv[4];
+            int bb[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int e = e0 + t;
-            while (q < nv && vidx[q] <= e) ++q;
-            vv[t] = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
-            bb[t] = rc.vb + q - 1;
+            for (int t = 0; t < 4; ++t) {
+                const int e = e0 + t;
+                while (q < nv && vidx[q] <= e) ++q;
+                vv[t] = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
+                bb[t] = rc.vb + q - 1;
+            }
+            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
         }
-        store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+    } else {
+        // many surviving vertices (a partly dense chunk): search the slot itself
+        const uint16_t* vx = ws.slot_idx + slot;
+        for (int g = 0; g < G; ++g) {
+            const int e0 = 4 * (g * NT + tid);
+            if (e0 >= len) break;
+            int lo = 0, hi = nv;
+            while (lo < hi) {
+                int mid = (lo + hi) >> 1;
+                if ((int)vx[mid] <= e0) lo = mid + 1;
+                else hi = mid;
+            }
+            int q = lo, qs = -1;
+            float sl = 0.0f;
+            float vv[4];
+            int bb[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = e0 + t;
+                while (q < nv && (int)vx[q] <= e) ++q;
+                if (q > 0 && q < nv && qs != q) {
+                    sl = edge_slope(q - 1);
+                    qs = q;
+                }
+                vv[t] = (q == 0) ? sin_ : (q == nv ? sout : sl);
+                bb[t] = rc.vb + q - 1;
+            }
+            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+        }
     }
 }
 

@@ -18,6 +18,7 @@ constexpr int kShortMax = 4096;
 constexpr int kQhMax = 64;          // vertices of a block hull built by quickhull
 constexpr int kQhLevels = 10;       // quickhull levels before the chains-and-merges fallback
 constexpr int kRedoGrid = 768;      // workgroups of the fallback chunk kernel (3 per CU)
+constexpr int kExpTile = 512;       // surviving vertices of a chunk the expansion keeps in LDS
 constexpr int kMergeNT = 1024;
 constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
 constexpr int kWinK = 16;           // hull vertices kept at each end of a chunk's window
@@ -107,6 +108,7 @@ struct LongWs {
     int32_t* gpre;        // [R*m] vertices before each segment of a group's list
     int32_t* root_n;      // [R] segments in the root list (desc_scr) of each row
     int32_t* redo_n;      // [1] chunks the first chunk kernel left over (reset by the expansion)
+    double* rslope;       // [R*m] slope of the root edge into each root segment (from the previous one)
     double* ck_S;         // [R*m*(kLongNT+1)] S at each thread's first point (and the chunk end)
     double* ck_W;         // (weighted only)
     // the call's inputs, for points recomputed from them

@@ -502,9 +502,18 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             if (WT) ws.st_W[rb + j] = lW[j];
         }
         root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired, slast, nullptr);
+        if (fast) {
+            // the root edge into each segment, from the group hull's entries
+            const double* aS = reinterpret_cast<const double*>(pool);
+            const double* aW = aS + G * E;
+            for (int i = tid + 1; i < nseg; i += NT) {
+                const int t = pre[i];
+                ws.rslope[rb + i] = (aS[t] - aS[t - 1]) / (aW[t] - aW[t - 1]);
+            }
+        }
         if (tid == 0) {
             ws.row_flag[row] = sflag;
-            ws.root_n[row] = nseg;
+            ws.root_n[row] = nseg | (fast ? kRootSlopes : 0);
         }
     }
 }
@@ -613,6 +622,8 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
                 R32[2 * sidx] = (uint32_t)c;
                 R16[4 * sidx + 2] = (uint16_t)tpos(ar.tag[t]);
                 vbl[sidx] = t;  // root vertices before the segment
+                // the root edge into the segment
+                if (t > 0) ws.rslope[rb + sidx] = (ar.S[t] - ar.S[t - 1]) / (ar.W[t] - ar.W[t - 1]);
             }
             if (en) R16[4 * sidx + 3] = (uint16_t)tpos(ar.tag[t]);
             carry += tot;
@@ -716,12 +727,12 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         if (WT) ws.st_W[rb + j] = gW[j / G] + c.y;
     }
     __syncthreads();
-    // prefix counts of the root list for the expansion's records
+    // prefix counts and edge slopes of the root list for the expansion's records
     root_prefixes<NT>(R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ired, rcbuf,
                       fast ? rcbuf + top_root_cap(ng, m) : nullptr);
     if (tid == 0) {
         ws.row_flag[row] = sflag;
-        ws.root_n[row] = nroot;
+        ws.root_n[row] = nroot | (fast ? kRootSlopes : 0);
     }
 }
 
