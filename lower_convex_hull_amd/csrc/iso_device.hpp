@@ -722,65 +722,108 @@ __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r
     return team_bridge(ar, l0, cL, r0, cR, lane, 64, 0, true);
 }
 
-// Merges the nodes of a compact-array tree level by level: node k of the
-// first level is entries k*E .. k*E+cnt[k]-1; at each level node a and node
-// a+span merge into node a, one wave per merge.  Leaves the root's hull in
-// entries 0..cnt[0]-1.
+// Merges the nodes of a compact-array tree: node k of the first level is
+// entries k*E .. k*E+cnt[k]-1; at level l (span 2^l) node a and node a+span
+// merge into node a, one wave per merge.  Leaves the root's hull in entries
+// 0..cnt[0]-1.  There is no workgroup barrier between levels: node a's merges
+// at every level belong to one wave (merge_owner), which records in ver[a]
+// (LDS, zeroed by the caller before its last barrier) how many levels node a
+// has been through; a merge waits only until its right node has been through
+// every level at which that node had a partner.  A wait is only ever for a
+// lower level, so every wait ends.
+// Merges the nodes of a compact-array tree: node k of the first level is
+// entries k*E .. k*E+cnt[k]-1; at level l (span 2^l) node a and node a+span
+// merge into node a, one wave per merge.  Leaves the root's hull in entries
+// 0..cnt[0]-1.  There is no workgroup barrier between levels: node a's merges
+// at every level belong to one wave, which records in ver[a] (LDS, zeroed by
+// the caller before its last barrier) how many levels node a has been
+// through; a merge waits only until its right node has been through every
+// level at which that node had a partner.  A wait is only ever for a lower
+// level, so every wait ends.  Nodes 4u .. 4u+3 belong to wave u mod NW, and
+// with 16 waves u's two bit pairs swap, so that the few merges of the upper
+// levels (u a multiple of 2, 4, 8) land on waves of different SIMDs (wave w
+// runs on SIMD w mod 4).
 template <int NT>
-__device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int nn, int E) {
+__device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_t* ver, int nn, int E) {
     constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-    for (int span = 1; span < nn; span <<= 1) {
-        const int nm = (nn - span + 2 * span - 1) / (2 * span);
-        for (int k = wid; k < nm; k += NW) {
-            const int a = 2 * k * span, b = a + span;
-            const int cL = cnt[a], cR = cnt[b];
-            const int2 br = wave_bridge(ar, a * E, cL, b * E, cR, lane);
-            team_move(ar, a * E, br.x, b * E, br.y, cR, lane, 64, true);
-            if (lane == 0) cnt[a] = br.x + 1 + cR - br.y;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int u0 = NW == 16 ? (((wid & 3) << 2) | (wid >> 2)) : wid;
+    int lv = 0;
+    for (int span = 1; span < nn; span <<= 1, ++lv) {
+        // this wave's merges of the level: a = 4*u0 + 4*NW*j + r, a multiple of 2*span
+        for (int a0 = 4 * u0; a0 < nn; a0 += 4 * NW) {
+            for (int r = 0; r < 4; r += 2) {
+                const int a = a0 + r, b = a + span;
+                if ((a & (2 * span - 1)) != 0 || b >= nn) continue;
+                // the last level below this one at which b merged with a partner
+                int need = 0;
+                for (int l2 = 0, s2 = 1; l2 < lv; ++l2, s2 <<= 1)
+                    if (b + s2 < nn) need = l2 + 1;
+                while (__hip_atomic_load(ver + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need)
+                    __builtin_amdgcn_s_sleep(1);
+                const int cL = cnt[a], cR = cnt[b];
+                const int2 br = wave_bridge(ar, a * E, cL, b * E, cR, lane);
+                team_move(ar, a * E, br.x, b * E, br.y, cR, lane, 64, true);
+                if (lane == 0) {
+                    cnt[a] = br.x + 1 + cR - br.y;
+                    __hip_atomic_store(ver + a, lv + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                wave_sync();  // the wave's next merge reads the count
+            }
         }
-        __syncthreads();
     }
+    __syncthreads();
 }
 
 // Prefix counts over a row's root list D of nroot segments (at most one per
 // chunk, in chunk order) for the reconstruction: vb[i] = root vertices before
 // segment i (block ids), and fs[j] = segments in chunks before chunk j, which
 // is the index of the first segment whose chunk is >= j.  rc (LDS, nroot
-// ints) receives the segments' chunks so that fs is a binary search; vb0, when
-// given, already holds vb (the compact-array path knows it).
+// ints) receives the segments' chunks so that fs is a binary search.
+// root_fs takes rc as filled (and published by a barrier) by the caller.
 template <int NT>
-__device__ __forceinline__ void root_prefixes(const uint2* D, int nroot, int m, int32_t* vb, int32_t* fs,
-                                              int* ired, int32_t* rc, const int32_t* vb0) {
-    const int tid = threadIdx.x;
-    int carry = 0;
-    for (int t0 = 0; t0 < nroot; t0 += NT) {
-        const int i = t0 + tid;
-        int v = 0;
-        if (i < nroot) {
-            const uint2 d = D[i];
-            rc[i] = dchunk(d);
-            v = dhi(d) - dlo(d) + 1;
-        }
-        if (vb0) {
-            if (i < nroot) vb[i] = vb0[i];
-            continue;
-        }
-        int tot;
-        const int xv = wg_excl_scan_int<NT>(v, ired, &tot);
-        if (i < nroot) vb[i] = carry + xv;
-        carry += tot;
-    }
-    __syncthreads();
-    for (int j = tid; j < m; j += NT) {
-        int lo = 0, hi = nroot;  // first segment whose chunk is >= j
+__device__ __forceinline__ void root_fs(int nroot, int m, int32_t* fs, const int32_t* rc) {
+    // each thread a run of consecutive chunks: one binary search for the
+    // first, then a step per chunk (a chunk holds at most one segment)
+    const int kc = (m + NT - 1) / NT;
+    const int c0 = min(m, (int)threadIdx.x * kc), c1 = min(m, c0 + kc);
+    if (c0 < c1) {
+        int lo = 0, hi = nroot;  // first segment whose chunk is >= c0
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (rc[mid] < j) lo = mid + 1;
+            if (rc[mid] < c0) lo = mid + 1;
             else hi = mid;
         }
-        fs[j] = lo;
+        for (int j = c0; j < c1; ++j) {
+            while (lo < nroot && rc[lo] < j) ++lo;
+            fs[j] = lo;
+        }
     }
+}
+
+template <int NT>
+__device__ __forceinline__ void root_prefixes(const uint2* D, int nroot, int m, int32_t* vb, int32_t* fs,
+                                              int* ired, int32_t* rc) {
+    const int tid = threadIdx.x;
+    // each thread a run of consecutive segments: their chunks, and vb by one
+    // workgroup scan of the runs' vertex counts
+    const int ks = (nroot + NT - 1) / NT;
+    const int i0 = min(nroot, tid * ks), i1 = min(nroot, i0 + ks);
+    int loc = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint2 d = D[i];
+        rc[i] = dchunk(d);
+        loc += dhi(d) - dlo(d) + 1;
+    }
+    int tot;
+    int x = wg_excl_scan_int<NT>(loc, ired, &tot);  // its barrier also publishes rc
+    for (int i = i0; i < i1; ++i) {
+        const uint2 d = D[i];
+        vb[i] = x;
+        x += dhi(d) - dlo(d) + 1;
+    }
+    root_fs<NT>(nroot, m, fs, rc);
 }
 
 // Bit of a row's root-segment count meaning that the merge stored the slope of

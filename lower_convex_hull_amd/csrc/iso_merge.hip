@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     constexpr size_t kFast = (size_t)G * E * (8 + 8 + 4);
     __shared__ __align__(16) unsigned char pool[kGen > kFast ? kGen : kFast];
     __shared__ double lS[G], lW[G];
-    __shared__ int32_t HC[G], CNT[G], pre[G + 1];
+    __shared__ int32_t HC[G], CNT[G], VER[G], pre[G + 1];
     __shared__ uint2 D[G], SCR[G];
     __shared__ int2 MI[G / 2 + 1];
     __shared__ int s_nhard;
@@ -328,17 +328,36 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     const int j0 = g * G, gc = min(G, m - j0);
     const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
 
-    // hull counts; the fast path needs every chunk hull whole in its window
-    int hc = 0;
-    if (tid < gc) {
-        hc = ws.hull_cnt[rb + j0 + tid];
-        HC[tid] = hc;
+    // the prelude's global reads, issued together: every chunk window (raw
+    // 16-byte words, the hull count in each header) and the chunk totals
+    constexpr int kW2 = (int)(sizeof(WinRec) / sizeof(double2));
+    constexpr int kRaw = (G * kW2 + NT - 1) / NT;
+    const int nraw = gc * kW2;
+    const double2* wsrc = reinterpret_cast<const double2*>(ws.win + rb + j0);
+    double2 raw[kRaw];
+#pragma unroll
+    for (int q = 0; q < kRaw; ++q) {
+        const int i = tid + q * NT;
+        raw[q] = i < nraw ? wsrc[i] : make_double2(0.0, 0.0);
     }
-    const bool fast = __syncthreads_and(tid >= gc || hc <= E) != 0;
+    double ts = 0.0, tw = 0.0;
+    if (wid == 0 && wlane < gc) {
+        ts = ws.tot_S[rb + j0 + wlane];
+        if (WT) tw = ws.tot_W[rb + j0 + wlane];
+    }
+    // hull counts; the fast path needs every chunk hull whole in its window
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < kRaw; ++q) {
+        const int i = tid + q * NT;
+        if (i < nraw && i % kW2 == 0) {
+            const int h = (int)(uint32_t)__double_as_longlong(raw[q].x);  // WinRec::h
+            HC[i / kW2] = h;
+            ok = ok && h <= E;
+        }
+    }
     if (wid == 0) {
         // chunk starts relative to the group: a scan of the chunk totals
-        double ts = wlane < gc ? ws.tot_S[rb + j0 + wlane] : 0.0;
-        double tw = (WT && wlane < gc) ? ws.tot_W[rb + j0 + wlane] : 0.0;
         double is = ts, iw = tw;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -356,7 +375,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         const double totS = __shfl(is, 63), totW = __shfl(iw, 63);
         if (wlane == 0) ws.gtot[row * ng + g] = make_double2(totS, WT ? totW : 0.0);
     }
-    __syncthreads();
+    const bool fast = __syncthreads_and(ok) != 0;
     const size_t sl = (size_t)(rb + j0) * (kChunk + 1);
     GroupWin* gwo = ws.gwin + row * ng + g;
     int nseg, hg;
@@ -364,21 +383,24 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         // ---- every chunk hull is short: merge compact arrays in LDS
         double* aS = reinterpret_cast<double*>(pool);
         const Arr ar{aS, aS + G * E, reinterpret_cast<int32_t*>(aS + 2 * G * E)};
-        for (int t = tid; t < gc * E; t += NT) {
-            const int i = t / E, e = t - i * E;
-            if (e < HC[i]) {
-                const double2 v = ws.win[rb + j0 + i].v[e];
-                ar.S[t] = lS[i] + v.x;
-                ar.W[t] = lW[i] + v.y;
+#pragma unroll
+        for (int q = 0; q < kRaw; ++q) {
+            const int r = tid + q * NT;
+            const int i = r / kW2, e = r - i * kW2 - 1;  // word 0 is the header
+            if (r < nraw && e >= 0 && e < HC[i]) {
+                const int t = i * E + e;
+                ar.S[t] = lS[i] + raw[q].x;
+                ar.W[t] = lW[i] + raw[q].y;
                 ar.tag[t] = mktag(i, e);
             }
         }
         for (int i = tid; i < gc; i += NT) {
             CNT[i] = HC[i];
+            VER[i] = 0;
             sfirst[i] = -1;
         }
         __syncthreads();
-        merge_arrays<NT>(ar, CNT, gc, E);
+        merge_arrays<NT>(ar, CNT, VER, gc, E);
         hg = CNT[0];
         // the group's list: one segment per run of a chunk's vertices
         for (int t = tid; t < hg; t += NT) {
@@ -412,10 +434,12 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         // ---- segment lists over the chunk hulls' windows
         WinRec* Wn = reinterpret_cast<WinRec*>(pool);
         {
-            const double2* src = reinterpret_cast<const double2*>(ws.win + rb + j0);
             double2* dst = reinterpret_cast<double2*>(Wn);
-            const int nv2 = gc * (int)(sizeof(WinRec) / sizeof(double2));
-            for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+#pragma unroll
+            for (int q = 0; q < kRaw; ++q) {
+                const int i = tid + q * NT;
+                if (i < nraw) dst[i] = raw[q];
+            }
         }
         for (int i = tid; i < gc; i += NT) {
             D[i] = mkdesc(i, 0, HC[i] - 1);
@@ -501,7 +525,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             ws.st_S[rb + j] = lS[j];
             if (WT) ws.st_W[rb + j] = lW[j];
         }
-        root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired, slast, nullptr);
+        root_prefixes<NT>(D, nseg, m, ws.vb + rb, ws.node_cnt + rb, ired, slast);
         if (fast) {
             // the root edge into each segment, from the group hull's entries
             const double* aS = reinterpret_cast<const double*>(pool);
@@ -520,16 +544,16 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
 
 // Dynamic LDS of the second stage: group starts gS, gW (8 B each), then
 // either the segment-list path's D, SCR (16 B each), GW, MI (8 B per merge),
-// CNT, GH (4 B each), or the compact-array path's 2 kGWinK entries per group
-// (S, W, tag) and CNT; after that the root segments' chunks and their vertex
-// prefix (at most one segment per chunk and one per window entry).
+// CNT (4 B each, and 4 B spare), or the compact-array path's 2 kGWinK entries
+// per group (S, W, tag) and CNT; after that the root segments' chunks (at most
+// one segment per chunk and one per window entry).
 __host__ __device__ inline size_t top_lds_main(int ng) {
     const size_t gen = (size_t)ng * (32 + sizeof(GroupWin) + 8) + (size_t)(ng / 2 + 1) * 8;
     const size_t fast = (size_t)ng * (2 * kGWinK) * 20 + (size_t)ng * 4;
     return (size_t)ng * 16 + (gen > fast ? gen : fast);
 }
 __host__ __device__ inline int top_root_cap(int ng, int m) { return m < ng * 2 * kGWinK ? m : ng * 2 * kGWinK; }
-inline size_t top_lds_bytes(int ng, int m) { return top_lds_main(ng) + (size_t)top_root_cap(ng, m) * 8; }
+inline size_t top_lds_bytes(int ng, int m) { return top_lds_main(ng) + (size_t)top_root_cap(ng, m) * 4; }
 
 template <bool WT>
 __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
@@ -539,43 +563,78 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     __shared__ int ired[NT / 64 + 1];
     __shared__ int s_nhard;
     __shared__ int4 s_hard[kHardCap];
-    __shared__ int sflag;
     __shared__ int s_ilo[kTopMax], s_ihi[kTopMax], s_off[kTopMax + 1];
+    __shared__ int s_gh[kTopMax], s_gn[kTopMax], s_gf[kTopMax], s_ver[kTopMax];
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m, gb = row * ng;
     const int tid = threadIdx.x;
 
-    // group hull counts; the fast path needs every group hull whole in its window
-    int hgv = 0, f = 0;
-    if (tid == 0) sflag = 0;
-    if (tid < ng) {
-        hgv = ws.gwin[gb + tid].h;
-        f = ws.gwin[gb + tid].flags;
+    // the prelude's global reads, issued together: every group window (raw
+    // 16-byte words; the header holds the hull count, segment count and data
+    // flags) and the group totals
+    constexpr int kW2 = (int)(sizeof(GroupWin) / sizeof(double2));
+    constexpr int kRaw = (kTopMax * kW2 + NT - 1) / NT;
+    const int nraw = ng * kW2;
+    const double2* wsrc = reinterpret_cast<const double2*>(ws.gwin + gb);
+    double2 raw[kRaw];
+#pragma unroll
+    for (int q = 0; q < kRaw; ++q) {
+        const int i = tid + q * NT;
+        raw[q] = i < nraw ? wsrc[i] : make_double2(0.0, 0.0);
     }
-    const bool fast = (__syncthreads_and(tid >= ng || hgv <= E) != 0) && ng <= kTopFastMax &&
-                      m < kTagMaxChunks;
-    if (f) atomicOr(&sflag, f);
-
-    // group starts (exclusive scan of the group totals)
-    double* gS = reinterpret_cast<double*>(top_lds);
-    double* gW = gS + ng;
-    double cS = 0.0, cW = 0.0;
-    for (int t0 = 0; t0 < ng; t0 += NT) {
-        const int g = t0 + tid;
-        const double2 gt = g < ng ? ws.gtot[gb + g] : make_double2(0.0, 0.0);
-        double tot;
-        const double xs = wg_excl_scan<NT>(gt.x, red, &tot);
-        if (g < ng) gS[g] = cS + xs;
-        cS += tot;
-        if (WT) {
-            const double xw = wg_excl_scan<NT>(gt.y, red, &tot);
-            if (g < ng) gW[g] = cW + xw;
-            cW += tot;
-        } else if (g < ng) {
-            gW[g] = (double)((int64_t)g * G * kChunk);
+    // the chunk starts relative to their groups (S only: unit weights), for
+    // the row's chunk starts stored at the end (a row has at most kTopMax
+    // groups of kGroup chunks)
+    constexpr int kRo = (kTopMax * kGroup + NT - 1) / NT;
+    double cstv[kRo];
+#pragma unroll
+    for (int q = 0; q < kRo; ++q) {
+        const int j = tid + q * NT;
+        if (!WT && j < m) cstv[q] = reinterpret_cast<const double*>(ws.cst + rb + j)[0];
+    }
+    const int wid = tid >> 6, lane = tid & 63;
+    double2 gt0 = make_double2(0.0, 0.0), gt1 = make_double2(0.0, 0.0);  // groups 2*lane, 2*lane+1
+    if (wid == 0) {
+        if (2 * lane < ng) gt0 = ws.gtot[gb + 2 * lane];
+        if (2 * lane + 1 < ng) gt1 = ws.gtot[gb + 2 * lane + 1];
+    }
+    // group hull counts; the fast path needs every group hull whole in its window
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < kRaw; ++q) {
+        const int i = tid + q * NT;
+        if (i < nraw && i % kW2 == 0) {
+            const uint64_t h01 = (uint64_t)__double_as_longlong(raw[q].x);  // h, nseg
+            const int h = (int)(uint32_t)h01;
+            s_gh[i / kW2] = h;
+            s_gn[i / kW2] = (int)(uint32_t)(h01 >> 32);
+            s_gf[i / kW2] = (int)(uint32_t)__double_as_longlong(raw[q].y);  // data flags
+            ok = ok && h <= E;
         }
     }
-    __syncthreads();
+
+    // group starts (exclusive scan of the group totals, two groups per lane)
+    double* gS = reinterpret_cast<double*>(top_lds);
+    double* gW = gS + ng;
+    if (wid == 0) {
+        double is = gt0.x + gt1.x, iw = gt0.y + gt1.y;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const double us = __shfl_up(is, d), uw = __shfl_up(iw, d);
+            if (lane >= d) { is += us; iw += uw; }
+        }
+        double es = __shfl_up(is, 1), ew = __shfl_up(iw, 1);
+        if (lane == 0) { es = 0.0; ew = 0.0; }
+        if (2 * lane < ng) {
+            gS[2 * lane] = es;
+            gW[2 * lane] = WT ? ew : (double)((int64_t)(2 * lane) * G * kChunk);
+        }
+        if (2 * lane + 1 < ng) {
+            gS[2 * lane + 1] = es + gt0.x;
+            gW[2 * lane + 1] = WT ? ew + gt0.y : (double)((int64_t)(2 * lane + 1) * G * kChunk);
+        }
+    }
+    const bool fast = (__syncthreads_and(ok) != 0) && ng <= kTopFastMax && m < kTagMaxChunks;
     uint2* R = ws.desc_scr + rb;  // the root list, as segments of chunk hulls
     // after both paths' LDS: the root segments' chunks (and, on the compact
     // path, their vertex prefix), for the record prefix counts
@@ -586,23 +645,36 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         double* aS = gW + ng;
         const Arr ar{aS, aS + ng * E, reinterpret_cast<int32_t*>(aS + 2 * ng * E)};
         int32_t* CNT = ar.tag + ng * E;
-        for (int t = tid; t < ng * E; t += NT) {
-            // every window entry is read (unused ones too), so the loads do not
-            // wait for the group's vertex count
-            const int g = t / E, e = t - g * E;
-            const GroupWin* gw = ws.gwin + gb + g;
-            const double2 v = gw->v[e];
-            const int tg = gw->tag[e];
-            ar.S[t] = gS[g] + v.x;
-            ar.W[t] = gW[g] + v.y;
-            ar.tag[t] = tg;
+        // words 1..E of a window are its entries' (S, W), the next E/4 words
+        // their tags, four to a word (unused entries are copied too)
+#pragma unroll
+        for (int q = 0; q < kRaw; ++q) {
+            const int r = tid + q * NT;
+            const int g = r / kW2, o = r - g * kW2;
+            if (r < nraw && o >= 1) {
+                if (o <= E) {
+                    const int t = g * E + o - 1;
+                    ar.S[t] = gS[g] + raw[q].x;
+                    ar.W[t] = gW[g] + raw[q].y;
+                } else {
+                    const int t = g * E + 4 * (o - 1 - E);
+                    const uint64_t x = (uint64_t)__double_as_longlong(raw[q].x);
+                    const uint64_t y = (uint64_t)__double_as_longlong(raw[q].y);
+                    ar.tag[t] = (int32_t)(uint32_t)x;
+                    ar.tag[t + 1] = (int32_t)(uint32_t)(x >> 32);
+                    ar.tag[t + 2] = (int32_t)(uint32_t)y;
+                    ar.tag[t + 3] = (int32_t)(uint32_t)(y >> 32);
+                }
+            }
         }
-        for (int g = tid; g < ng; g += NT) CNT[g] = ws.gwin[gb + g].h;
+        for (int g = tid; g < ng; g += NT) {
+            CNT[g] = s_gh[g];
+            s_ver[g] = 0;
+        }
         __syncthreads();
-        merge_arrays<NT>(ar, CNT, ng, E);
+        merge_arrays<NT>(ar, CNT, s_ver, ng, E);
         const int hr = CNT[0];
-        // one root segment per run of a chunk's vertices
-        int32_t* vbl = rcbuf + top_root_cap(ng, m);  // after the chunk-id buffer
+        // one root segment per run of a chunk's vertices; its chunk into rcbuf
         uint16_t* R16 = reinterpret_cast<uint16_t*>(R);
         uint32_t* R32 = reinterpret_cast<uint32_t*>(R);
         int carry = 0;
@@ -621,7 +693,8 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             if (st) {
                 R32[2 * sidx] = (uint32_t)c;
                 R16[4 * sidx + 2] = (uint16_t)tpos(ar.tag[t]);
-                vbl[sidx] = t;  // root vertices before the segment
+                rcbuf[sidx] = c;
+                ws.vb[rb + sidx] = t;  // root vertices before the segment
                 // the root edge into the segment
                 if (t > 0) ws.rslope[rb + sidx] = (ar.S[t] - ar.S[t - 1]) / (ar.W[t] - ar.W[t - 1]);
             }
@@ -636,17 +709,17 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         GroupWin* GW = reinterpret_cast<GroupWin*>(SCR + ng);
         int2* MI = reinterpret_cast<int2*>(GW + ng);
         int32_t* CNT = reinterpret_cast<int32_t*>(MI + (ng / 2 + 1));
-        int32_t* GH = CNT + ng;
+        const int32_t* GH = s_gh;
         {
-            const double2* src = reinterpret_cast<const double2*>(ws.gwin + gb);
             double2* dst = reinterpret_cast<double2*>(GW);
-            const int nv2 = ng * (int)(sizeof(GroupWin) / sizeof(double2));
-            for (int i = tid; i < nv2; i += NT) dst[i] = src[i];
+#pragma unroll
+            for (int q = 0; q < kRaw; ++q) {
+                const int i = tid + q * NT;
+                if (i < nraw) dst[i] = raw[q];
+            }
         }
-        __syncthreads();
         for (int g = tid; g < ng; g += NT) {
-            GH[g] = GW[g].h;
-            D[g] = make_int4(g, 0, GW[g].h - 1, 0);
+            D[g] = make_int4(g, 0, GH[g] - 1, 0);
             CNT[g] = 1;
         }
         __syncthreads();
@@ -677,7 +750,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         const int nr2 = CNT[0];
         auto seg_of = [&](int g, int p) {
             const int base = g * G;
-            int a = 0, b = GW[g].nseg - 1;
+            int a = 0, b = s_gn[g] - 1;
             while (a < b) {
                 const int mid = (a + b + 1) >> 1;
                 if (ws.gpre[rb + base + mid] <= p) a = mid;
@@ -690,48 +763,98 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             // a whole group list (always so where every merge was convex)
             // needs no search
             s_ilo[t] = d.y == 0 ? 0 : (d.y == 1 ? (ws.gpre[rb + d.x * G + 1] > 1 ? 0 : 1) : seg_of(d.x, d.y));
-            s_ihi[t] = d.z == GH[d.x] - 1 ? GW[d.x].nseg - 1 : seg_of(d.x, d.z);
+            s_ihi[t] = d.z == GH[d.x] - 1 ? s_gn[d.x] - 1 : seg_of(d.x, d.z);
         }
         __syncthreads();
-        if (tid == 0) {
-            int o = 0;
-            for (int t = 0; t < nr2; ++t) {
-                s_off[t] = o;
-                o += s_ihi[t] - s_ilo[t] + 1;
+        if (wid == 0) {
+            // s_off: root segments before each root entry (two entries a lane)
+            const int t0 = 2 * lane, t1 = t0 + 1;
+            const int v0 = t0 < nr2 ? s_ihi[t0] - s_ilo[t0] + 1 : 0;
+            const int v1 = t1 < nr2 ? s_ihi[t1] - s_ilo[t1] + 1 : 0;
+            int x = v0 + v1;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(x, d);
+                if (lane >= d) x += u;
             }
-            s_off[nr2] = o;
+            const int ex = x - v0 - v1;
+            if (t0 <= nr2) s_off[t0] = ex;
+            if (t1 <= nr2) s_off[t1] = ex + v0;
         }
         __syncthreads();
         nroot = s_off[nr2];
-        for (int o = tid; o < nroot; o += NT) {
-            int a = 0, b = nr2 - 1;
-            while (a < b) {
-                const int mid = (a + b + 1) >> 1;
-                if (s_off[mid] <= o) a = mid;
-                else b = mid - 1;
+        // each thread a run of consecutive root segments (at most kRo, as a
+        // row has at most one per chunk): every load first, then the
+        // segments, their chunks (rcbuf) and vertex counts, and vb by one
+        // workgroup scan
+        const int ks = (nroot + NT - 1) / NT;
+        const int o0 = min(nroot, tid * ks), no = min(nroot, o0 + ks) - o0;
+        int4 ddv[kRo];
+        uint2 dv[kRo];
+        int iv[kRo], pv[kRo], av[kRo];
+#pragma unroll
+        for (int q = 0; q < kRo; ++q) {
+            const int o = o0 + q;
+            if (q < no) {
+                int a = 0, b = nr2 - 1;
+                while (a < b) {
+                    const int mid = (a + b + 1) >> 1;
+                    if (s_off[mid] <= o) a = mid;
+                    else b = mid - 1;
+                }
+                av[q] = a;
+                ddv[q] = D[a];
+                iv[q] = s_ilo[a] + (o - s_off[a]);
+                const int k = ddv[q].x * G + iv[q];
+                dv[q] = ws.desc[rb + k];
+                pv[q] = ws.gpre[rb + k];
             }
-            const int4 dd = D[a];
-            const int i = s_ilo[a] + (o - s_off[a]);
-            const int base = dd.x * G;
-            const uint2 d = ws.desc[rb + base + i];
-            const int pre_i = ws.gpre[rb + base + i];
-            const int lo = i == s_ilo[a] ? dlo(d) + (dd.y - pre_i) : dlo(d);
-            const int hi = i == s_ihi[a] ? dlo(d) + (dd.z - pre_i) : dhi(d);
-            R[o] = mkdesc(dchunk(d), lo, hi);
+        }
+        int loc = 0, len[kRo];
+#pragma unroll
+        for (int q = 0; q < kRo; ++q) {
+            const int o = o0 + q;
+            len[q] = 0;
+            if (q < no) {
+                const int a = av[q], i = iv[q];
+                const uint2 d = dv[q];
+                const int lo = i == s_ilo[a] ? dlo(d) + (ddv[q].y - pv[q]) : dlo(d);
+                const int hi = i == s_ihi[a] ? dlo(d) + (ddv[q].z - pv[q]) : dhi(d);
+                R[o] = mkdesc(dchunk(d), lo, hi);
+                rcbuf[o] = dchunk(d);
+                len[q] = hi - lo + 1;
+                loc += len[q];
+            }
+        }
+        int tot;
+        int x = wg_excl_scan_int<NT>(loc, ired, &tot);
+#pragma unroll
+        for (int q = 0; q < kRo; ++q) {
+            if (q < no) ws.vb[rb + o0 + q] = x;
+            x += len[q];
         }
     }
     // chunk starts of the row: group start plus the chunk's start in its group
-    for (int j = tid; j < m; j += NT) {
-        const double2 c = ws.cst[rb + j];
-        ws.st_S[rb + j] = gS[j / G] + c.x;
-        if (WT) ws.st_W[rb + j] = gW[j / G] + c.y;
+#pragma unroll
+    for (int q = 0; q < kRo; ++q) {
+        const int j = tid + q * NT;
+        if (j < m) {
+            if (WT) {
+                const double2 c = ws.cst[rb + j];
+                ws.st_S[rb + j] = gS[j / G] + c.x;
+                ws.st_W[rb + j] = gW[j / G] + c.y;
+            } else {
+                ws.st_S[rb + j] = gS[j / G] + cstv[q];
+            }
+        }
     }
     __syncthreads();
-    // prefix counts and edge slopes of the root list for the expansion's records
-    root_prefixes<NT>(R, nroot, m, ws.vb + rb, ws.node_cnt + rb, ired, rcbuf,
-                      fast ? rcbuf + top_root_cap(ng, m) : nullptr);
+    // the first root segment of each chunk, for the expansion's records
+    root_fs<NT>(nroot, m, ws.node_cnt + rb, rcbuf);
     if (tid == 0) {
-        ws.row_flag[row] = sflag;
+        int f = 0;
+        for (int g = 0; g < ng; ++g) f |= s_gf[g];
+        ws.row_flag[row] = f;
         ws.root_n[row] = nroot | (fast ? kRootSlopes : 0);
     }
 }
