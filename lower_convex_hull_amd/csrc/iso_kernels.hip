@@ -71,25 +71,42 @@ struct HullSmem {
     double pW[WT ? NP : 1];
     int32_t qk[2][NQ];
     double qS[2][NQ], qW[2][NQ];
-    unsigned long long qkey[NQ];
-    int qn, qcur, qstate;
+    unsigned long long qkey[2][NQ];
+    int qn, qcur;
 };
 
-// Exclusive and inclusive workgroup scans of one f64 value per thread.  The
+// A DPP move of an f64 within the wave (both 32-bit halves): lanes whose
+// source lies outside the pattern, or whose row is not in RM, read +0.0.
+template <int CTRL, int RM>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const long long u = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, RM, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, RM, 0xf, true);
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Inclusive f64 scan over the wave by DPP row shifts and row broadcasts
+// (adding +0.0 where a lane has no source leaves its value unchanged).
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+    x += dpp_f64<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_f64<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_f64<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_f64<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_f64<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Exclusive and inclusive workgroup scans of one f64 value per thread.  A
+// lane's exclusive value is the previous lane's inclusive one, moved, and the
 // wave totals are added in wave order, so thread L's inclusive value is
 // bit-identical to thread L+1's exclusive value.
 template <int NT>
 __device__ __forceinline__ void wg_scan2(double v, double* red, double& excl, double& incl) {
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    double x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double t = __shfl_up(x, d);
-        if (lane >= d) x += t;
-    }
-    double ex = __shfl_up(x, 1);
-    if (lane == 0) ex = 0.0;
+    const double x = wave_incl_scan_f64(v);
+    const double ex = dpp_f64<0x138, 0xf>(x);  // wave_shr:1 (lane 0 reads +0.0)
     if (lane == 63) red[wid] = x;
     __syncthreads();
     double before = 0.0;
@@ -279,115 +296,145 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             sm.qW[0][1] = sm.end_w;
             sm.qn = 2;
             sm.qcur = 0;
-            sm.qstate = 0;
         }
-        if (L < kQhMax) sm.qkey[L] = 0ull;
+        if (L < kQhMax) {
+            sm.qkey[0][L] = 0ull;
+            sm.qkey[1][L] = 0ull;
+        }
+        // this thread's chord, the one over point base (vertex ci <= base <
+        // vertex ci+1): its ends A, B and B's index kB, kept in registers from
+        // level to level; the list's size nv and buffer cb (the same in every
+        // thread); the keys of a level in buffer lv & 1
+        int ci = 0, kB = len, nv = 2, cb = 0, state = 0;
+        Pt A{0.0, 0.0}, B{sm.end_w, sm.end_s};
         __syncthreads();
         for (int lv = 0; lv < kQhLevels; ++lv) {
-            const int cb = sm.qcur, nv = sm.qn;
+            unsigned long long* qkey = sm.qkey[lv & 1];
             const int32_t* vk = sm.qk[cb];
-            int qi = 0;                       // this thread's last chord
+            int qi = ci;                      // this thread's last chord
             unsigned long long qbest = 0ull;  // and its best key there
             if (alive) {
-                // the chord over this thread's first point: vk[i] <= base < vk[i+1]
-                int i = 0, hi = nv - 1;
-                while (hi - i > 1) {
-                    const int mid = (i + hi) >> 1;
-                    if (vk[mid] <= base) i = mid;
-                    else hi = mid;
-                }
-                // chord i runs from vertex vk[i] to vertex nk; reloaded only
-                // when this thread's points pass a vertex (a point that became
-                // a vertex lies on its chords and drops out)
-                int nk = vk[i + 1];
-                Pt A{sm.qW[cb][i], sm.qS[cb][i]}, B{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
                 double bc = 0.0;
                 int bk = 0;
-                for (uint32_t mm = alive; mm; mm &= mm - 1u) {
-                    const int b = lsb32(mm);
-                    const int k = base + b + 1;
-                    if (k >= nk) {
-                        if (bk) atomicMax(&sm.qkey[i], mkkey(bc, bk));
-                        bc = 0.0;
-                        bk = 0;
-                        do {
-                            ++i;
-                            nk = vk[i + 1];
-                        } while (nk <= k);
-                        A = Pt{sm.qW[cb][i], sm.qS[cb][i]};
-                        B = Pt{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
-                    }
-                    const Pt Pk{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
-                    const double c = cross3(A, Pk, B);
-                    if (c > 0.0) {
-                        if (c > bc) {
-                            bc = c;
-                            bk = k;
+                if (lv == 0) {
+                    // one chord, from point 0 to point len: the thread's own
+                    // points, from registers
+#pragma unroll
+                    for (int b = 0; b < P; ++b) {
+                        if ((alive >> b) & 1u) {
+                            const int k = base + b + 1;
+                            const Pt Pk{WT ? pw[b] : (double)k, ps[b]};
+                            const double c = cross3(A, Pk, B);
+                            if (c > 0.0) {
+                                if (c > bc) {
+                                    bc = c;
+                                    bk = k;
+                                }
+                            } else {
+                                alive &= ~(1u << b);
+                            }
                         }
-                    } else {
-                        alive &= ~(1u << b);
                     }
+                } else {
+                    // chord i runs from A to B (index nk); the next chords come
+                    // from the list when this thread's points pass a vertex
+                    // (a point that became a vertex lies on its chords and
+                    // drops out)
+                    int i = ci, nk = kB;
+                    Pt Ac = A, Bc = B;
+                    for (uint32_t mm = alive; mm; mm &= mm - 1u) {
+                        const int b = lsb32(mm);
+                        const int k = base + b + 1;
+                        if (k >= nk) {
+                            if (bk) atomicMax(&qkey[i], mkkey(bc, bk));
+                            bc = 0.0;
+                            bk = 0;
+                            do {
+                                ++i;
+                                nk = vk[i + 1];
+                            } while (nk <= k);
+                            Ac = Pt{sm.qW[cb][i], sm.qS[cb][i]};
+                            Bc = Pt{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
+                        }
+                        const Pt Pk{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
+                        const double c = cross3(Ac, Pk, Bc);
+                        if (c > 0.0) {
+                            if (c > bc) {
+                                bc = c;
+                                bk = k;
+                            }
+                        } else {
+                            alive &= ~(1u << b);
+                        }
+                    }
+                    qi = i;
                 }
-                qi = i;
                 qbest = bk ? mkkey(bc, bk) : 0ull;
             }
-            {
-                // one atomic per wave when all of its threads with a candidate
-                // ended on the same chord (always so at the first level)
-                const uint64_t act = __ballot(qbest != 0ull);
-                if (act) {
-                    const int lane = threadIdx.x & 63;
-                    const int first = __ffsll((long long)act) - 1;
-                    const int fi = __shfl(qi, first);
-                    if (__ballot(qbest != 0ull && qi != fi) == 0) {
-                        unsigned long long mx = qbest;
-#pragma unroll
-                        for (int d = 1; d < 64; d <<= 1) {
-                            const unsigned long long o = __shfl_xor(mx, d);
-                            mx = o > mx ? o : mx;  // threads without a candidate hold 0
-                        }
-                        if (lane == first) atomicMax(&sm.qkey[fi], mx);
-                    } else if (qbest) {
-                        atomicMax(&sm.qkey[qi], qbest);
-                    }
-                }
-            }
+            if (qbest) atomicMax(&qkey[qi], qbest);
             __syncthreads();
+            // every wave reads the chords' keys: which chords found a point
+            // (the same in every wave, so every thread takes the same exit)
+            const int lane = L & 63;
+            const unsigned long long kl = lane < nv - 1 ? qkey[lane] : 0ull;
+            const uint64_t bal = __ballot(kl != 0ull);
+            const int add = __popcll(bal);
+            if (add == 0) {
+                state = 1;  // no point left below any chord: done
+                break;
+            }
+            if (nv + add > kQhMax) {
+                state = 2;  // too many vertices: fall back
+                break;
+            }
             if (L < 64) {
-                // one wave inserts each chord's farthest point after the
-                // chord's start, its coordinates from the staged points
-                const bool found = L < nv - 1 && sm.qkey[L] != 0ull;
-                const uint64_t bal = __ballot(found);
+                // wave 0 writes the new list, each chord's point after the
+                // chord's start (coordinates from the staged points), and
+                // clears the other key buffer (last read a level ago)
                 const int pre = __popcll(bal & ((1ull << L) - 1ull));
-                const int add = __popcll(bal);
                 const int nb = 1 - cb;
-                if (nv + add <= kQhMax && L < nv) {
+                if (L < nv) {
                     sm.qk[nb][L + pre] = vk[L];
                     sm.qS[nb][L + pre] = sm.qS[cb][L];
                     sm.qW[nb][L + pre] = sm.qW[cb][L];
-                    if (found) {
-                        const int k = (int)(0x1fff - (sm.qkey[L] & 0x1fffull));
+                    if (kl) {
+                        const int k = (int)(0x1fff - (kl & 0x1fffull));
                         sm.qk[nb][L + pre + 1] = k;
                         sm.qS[nb][L + pre + 1] = pS[sk(k)];
                         sm.qW[nb][L + pre + 1] = WT ? pW[sk(k)] : (double)k;
                     }
                 }
-                if (L < kQhMax) sm.qkey[L] = 0ull;
+                sm.qkey[(lv & 1) ^ 1][L] = 0ull;
                 if (L == 0) {
-                    if (add == 0) {
-                        sm.qstate = 1;  // no point left below any chord: done
-                    } else if (nv + add > kQhMax) {
-                        sm.qstate = 2;  // too many vertices: fall back
-                    } else {
-                        sm.qn = nv + add;
-                        sm.qcur = nb;
-                    }
+                    sm.qn = nv + add;
+                    sm.qcur = nb;
                 }
             }
+            if (alive) {
+                // this thread's chord in the new list: the half of the old
+                // one that holds point base
+                const unsigned long long kc = qkey[ci];
+                const int pre = __popcll(bal & ((1ull << ci) - 1ull));
+                if (kc) {
+                    const int k = (int)(0x1fff - (kc & 0x1fffull));
+                    const Pt K{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
+                    if (k <= base) {
+                        A = K;
+                        ci += pre + 1;
+                    } else {
+                        B = K;
+                        kB = k;
+                        ci += pre;
+                    }
+                } else {
+                    ci += pre;
+                }
+            }
+            nv += add;
+            cb = 1 - cb;
             __syncthreads();
-            if (sm.qstate != 0) break;
         }
-        if (sm.qstate == 1) {
+        if (state == 1) {
             // the vertex list, made convex as computed (a near-tie may have
             // picked a point that is not quite the farthest)
             const int cb = sm.qcur, nv = sm.qn;
