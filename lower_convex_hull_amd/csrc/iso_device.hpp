@@ -832,32 +832,37 @@ constexpr int kRootSlopes = 1 << 30;
 
 // The reconstruction record of chunk j (Corollary 4.5) from the root list and
 // its prefix counts: the range of the chunk's surviving hull vertices and the
-// slopes of the edges into and out of it, or the one edge it lies under.  The
-// edge slopes come from rslope when the merge stored them, else from the
-// vertices (X).
+// slopes of the edges into and out of it, or the one edge it lies under.  i is
+// the first root segment whose chunk is >= j.  The edge slopes come from
+// rslope when the merge stored them, else from the vertices (X).  Every load
+// the record may need is issued before any is used.
 template <class V>
 __device__ __forceinline__ ChunkRec chunk_record(const V X, const uint2* D, int nroot_bits,
-                                                 const int32_t* vb, const int32_t* fs,
-                                                 const double* rslope, int j) {
+                                                 const int32_t* vb, int i, const double* rslope, int j) {
     const bool have = (nroot_bits & kRootSlopes) != 0;
     const int nroot = nroot_bits & ~kRootSlopes;
-    const int i = fs[j];  // first root segment with chunk >= j
     const int ic = min(i, nroot - 1);
     const uint2 d = D[ic];
-    ChunkRec rc;
-    rc.pad = 0;
-    rc.vb = vb[ic];
-    auto slope_into = [&](int s) {  // the root edge into segment s >= 1
-        if (have) return rslope[s];
-        const uint2 p = D[s - 1], q = D[s];
+    const uint2 dp = D[max(ic - 1, 0)];
+    const uint2 dn = D[min(ic + 1, nroot - 1)];
+    const int vbi = vb[ic];
+    double r_in = 0.0, r_out = 0.0;
+    if (have) {
+        r_in = rslope[max(ic, 1)];
+        r_out = rslope[min(ic + 1, nroot - 1)];
+    }
+    auto vslope = [&](uint2 p, uint2 q) {  // the root edge from segment p's end to q's start
         const Pt A = X.vtx(dchunk(p), dhi(p), j), B = X.vtx(dchunk(q), dlo(q), j);
         return (B.s - A.s) / (B.w - A.w);
     };
+    ChunkRec rc;
+    rc.pad = 0;
+    rc.vb = vbi;
     if (i < nroot && dchunk(d) == j) {
         rc.lo = dlo(d);
         rc.hi = dhi(d);
-        rc.slope_in = i > 0 ? slope_into(i) : 0.0;
-        rc.slope_out = i + 1 < nroot ? slope_into(i + 1) : 0.0;
+        rc.slope_in = i > 0 ? (have ? r_in : vslope(dp, d)) : 0.0;
+        rc.slope_out = i + 1 < nroot ? (have ? r_out : vslope(d, dn)) : 0.0;
     } else {
         // the chunk lies under one edge, from the last vertex of the previous
         // segment to the first vertex of the next (chunk 0 always holds the
@@ -865,7 +870,7 @@ __device__ __forceinline__ ChunkRec chunk_record(const V X, const uint2* D, int 
         // so i < nroot)
         rc.lo = -1;
         rc.hi = -1;
-        rc.slope_in = slope_into(i);
+        rc.slope_in = have ? r_in : vslope(dp, d);
         rc.slope_out = rc.slope_in;
     }
     return rc;

@@ -837,15 +837,15 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_redo(const float* __restrict_
 // it (paper equation (3), section 3.4).
 // ----------------------------------------------------------------------------
 template <bool WT>
-__global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
-                                                    float* __restrict__ out,
-                                                    int32_t* __restrict__ block_id, int rec_done) {
-    constexpr int NT = kLongNT, C = kChunk;
+__global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
+                                                   float* __restrict__ out,
+                                                   int32_t* __restrict__ block_id, int rec_done) {
+    constexpr int NT = kExpNT, C = kChunk;
     constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
     __shared__ int vidx[kExpTile + 1];
     __shared__ float vslope[kExpTile + 1];
     __shared__ ChunkRec s_rc;
-    __shared__ int s_inc;
+    __shared__ int s_inc, s_nan;
     const int64_t gid = blockIdx.x;
     const int64_t row = gid / m;
     const int j = (int)(gid - row * m);
@@ -871,7 +871,33 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         }
     };
     if (gid == 0 && tid == 0) *ws.redo_n = 0;  // for the next call's chunk kernels
-    if (ws.row_flag[row] & kFlagNonfinite) {
+    if (tid == 0) {
+        // the row's flags, the chunk's flags and its first root segment, read
+        // together; then the record
+        const int64_t rb = row * m;
+        const int rf = ws.row_flag[row];
+        const int cf = ws.chunk_flag[gid];
+        const int fsj = rec_done ? 0 : ws.node_cnt[rb + j];
+        const int nrb = rec_done ? 0 : ws.root_n[row];
+        ChunkRec r{};
+        if (rf & kFlagNonfinite) {
+            // the row comes out NaN: no record
+        } else if (rec_done) {
+            r = ws.rec[gid];
+        } else {
+            // this chunk's record from the row's root list (Corollary 4.5)
+            const size_t sl = (size_t)rb * (C + 1);
+            const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                            ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
+                            inc_src(ws, row, m, 0)};
+            r = chunk_record(X, ws.desc_scr + rb, nrb, ws.vb + rb, fsj, ws.rslope + rb, j);
+        }
+        s_rc = r;
+        s_inc = (cf & kChunkInc) != 0;
+        s_nan = (rf & kFlagNonfinite) != 0;
+    }
+    __syncthreads();
+    if (s_nan) {
         const float nan = __builtin_nanf("");
         for (int g = 0; g < G; ++g) {
             int e = 4 * (g * NT + tid);
@@ -879,22 +905,6 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         }
         return;
     }
-    if (tid == 0) {
-        if (rec_done) {
-            s_rc = ws.rec[gid];
-        } else {
-            // this chunk's record from the row's root list (Corollary 4.5)
-            const int64_t rb = row * m;
-            const size_t sl = (size_t)rb * (C + 1);
-            const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
-                            ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT,
-                            inc_src(ws, row, m, 0)};
-            s_rc = chunk_record(X, ws.desc_scr + rb, ws.root_n[row], ws.vb + rb, ws.node_cnt + rb,
-                                ws.rslope + rb, j);
-        }
-        s_inc = (ws.chunk_flag[gid] & kChunkInc) != 0;
-    }
-    __syncthreads();
     const ChunkRec rc = s_rc;
     if (rc.lo < 0) {
         const float v = sign * (float)rc.slope_in;
@@ -914,17 +924,25 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         const float* gy = ws.y + off;
         const bool vy = vec && (((uintptr_t)gy) & 15u) == 0;
         const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
+        // every load first, then the stores
+        float4 ya[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int e0 = 4 * (g * NT + tid);
+            if (vy && e0 + 4 <= len) {
+                ya[g] = *reinterpret_cast<const float4*>(gy + e0);
+            } else {
+                ya[g].x = e0 < len ? gy[e0] : 0.0f;
+                ya[g].y = e0 + 1 < len ? gy[e0 + 1] : 0.0f;
+                ya[g].z = e0 + 2 < len ? gy[e0 + 2] : 0.0f;
+                ya[g].w = e0 + 3 < len ? gy[e0 + 3] : 0.0f;
+            }
+        }
+#pragma unroll
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
             if (e0 >= len) break;
-            float yy[4];
-            if (vy && e0 + 4 <= len) {
-                const float4 v = *reinterpret_cast<const float4*>(gy + e0);
-                yy[0] = v.x; yy[1] = v.y; yy[2] = v.z; yy[3] = v.w;
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) yy[t] = e0 + t < len ? gy[e0 + t] : 0.0f;
-            }
+            const float yy[4] = {ya[g].x, ya[g].y, ya[g].z, ya[g].w};
             float vv[4];
             int bb[4];
 #pragma unroll
@@ -950,17 +968,24 @@ __global__ __launch_bounds__(kLongNT) void k_expand(int64_t n, int m, float sign
         for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
         for (int v = tid; v + 1 < nv; v += NT) vslope[v] = edge_slope(v);
         __syncthreads();
+        // q = number of the chunk's surviving vertices at or before each
+        // group's first element: the groups' searches step together, one LDS
+        // round trip per halving
+        int qg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) qg[g] = 0;
+        for (int stp = 1 << (31 - __clz(nv)); stp > 0; stp >>= 1) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int e0 = 4 * (g * NT + tid);
+                if (qg[g] + stp <= nv && vidx[qg[g] + stp - 1] <= e0) qg[g] += stp;
+            }
+        }
+#pragma unroll
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
             if (e0 >= len) break;
-            // q = number of the chunk's surviving vertices at or before e0
-            int lo = 0, hi = nv;
-            while (lo < hi) {
-                int mid = (lo + hi) >> 1;
-                if (vidx[mid] <= e0) lo = mid + 1;
-                else hi = mid;
-            }
-            int q = lo;
+            int q = qg[g];
             float vv[4];
             int bb[4];
 #pragma unroll
@@ -1063,10 +1088,10 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
     if (e != hipSuccess) return e;
     timed_begin(kPhaseExpand, st);
     if (wt)
-        hipLaunchKernelGGL(k_expand<true>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign, ws,
+        hipLaunchKernelGGL(k_expand<true>, dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign, ws,
                            out, block_id, (int)rec_done);
     else
-        hipLaunchKernelGGL(k_expand<false>, dim3(nblk), dim3(kLongNT), 0, st, sh.n, sh.m, sh.sign,
+        hipLaunchKernelGGL(k_expand<false>, dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign,
                            ws, out, block_id, (int)rec_done);
     timed_end(st);
     return hipGetLastError();

@@ -19,6 +19,7 @@ constexpr int kQhMax = 64;          // vertices of a block hull built by quickhu
 constexpr int kQhLevels = 10;       // quickhull levels before the chains-and-merges fallback
 constexpr int kRedoGrid = 768;      // workgroups of the fallback chunk kernel (3 per CU)
 constexpr int kExpTile = 512;       // surviving vertices of a chunk the expansion keeps in LDS
+constexpr int kExpNT = 128;        // threads of an expansion workgroup (one chunk, 32 elements each)
 constexpr int kMergeNT = 1024;
 constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
 constexpr int kWinK = 16;           // hull vertices kept at each end of a chunk's window
