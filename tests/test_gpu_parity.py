@@ -204,6 +204,21 @@ def test_mixed_dense_and_noisy_stretches(torch):
     check(torch, y, w, name="mixed-w/2.4e6", block_ids=False)
 
 
+def test_rows_with_many_groups(torch):
+    """Rows of 60 groups of 64 chunks: the second merge stage holds only part
+    of its group windows in registers and reads the rest where it uses them
+    (unit weights and weighted, compact-array and segment-list paths)."""
+    n = 60 * 64 * 4096 - 777
+    y, _ = inputs.noisy(1, n, 35)
+    check(torch, y, None, name="noisy/60 groups", block_ids=False)
+    w = inputs.weights("exp", n, 36)[None, :]
+    check(torch, y, w, name="noisy-w/60 groups", block_ids=False)
+    d, _ = inputs.dense(n, 37)
+    d = d.copy()
+    d[0, n // 3] = -50.0  # one cliff: group hulls too long for their windows
+    check(torch, d, None, name="dense-cliff/60 groups", block_ids=False)
+
+
 def test_row_beyond_two_stage_merge(torch):
     """A row with more groups than the two-stage merge keeps in LDS: one
     workgroup merges every level with its lists in the workspace."""
