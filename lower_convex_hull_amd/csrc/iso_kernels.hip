@@ -141,6 +141,8 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     float wv[P];
     int bad = 0;
     if (threadIdx.x == 0) sm.flag = 0;
+    // a full block (no padding) takes loops without per-element range tests
+    const bool full = len == NT * P;
 
     // ---- load (each thread its P consecutive elements) and check the data
     float yr[P], wr[P];
@@ -167,21 +169,34 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     float yp = (L > 0 && base <= len) ? gy[base - 1] : 0.0f;
     if (!isfinite(yp)) yp = 0.0f;
     yp *= sign;
+    if (full) {
 #pragma unroll
-    for (int b = 0; b < P; ++b) {
-        int e = base + b;
-        bool in = e < len;
-        float yy = yr[b];
-        float ww = 1.0f;
-        if (WT) ww = wr[b];
-        if (in) {
+        for (int b = 0; b < P; ++b) {
+            float yy = yr[b];
+            float ww = 1.0f;
+            if (WT) ww = wr[b];
             if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
             if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
-        } else {
-            ww = 0.0f;
+            yv[b] = sign * yy;
+            wv[b] = ww;
         }
-        yv[b] = sign * yy;
-        wv[b] = ww;
+    } else {
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            int e = base + b;
+            bool in = e < len;
+            float yy = yr[b];
+            float ww = 1.0f;
+            if (WT) ww = wr[b];
+            if (in) {
+                if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
+                if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
+            } else {
+                ww = 0.0f;
+            }
+            yv[b] = sign * yy;
+            wv[b] = ww;
+        }
     }
 
     // ---- prefix sums (paper section 2.1, equation (2)), in f64
@@ -216,11 +231,18 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     s0 = xs;
     w0 = WT ? xw : (double)min(base, len);
     // point len: padding points (beyond len) become exact copies of it
+    if (full) {
+        if (L == NT - 1) {
+            sm.end_s = ps[P - 1];
+            sm.end_w = WT ? pw[P - 1] : (double)len;
+        }
+    } else {
 #pragma unroll
-    for (int b = 0; b < P; ++b) {
-        if (base + b + 1 == len) {
-            sm.end_s = ps[b];
-            sm.end_w = WT ? pw[b] : (double)len;
+        for (int b = 0; b < P; ++b) {
+            if (base + b + 1 == len) {
+                sm.end_s = ps[b];
+                sm.end_w = WT ? pw[b] : (double)len;
+            }
         }
     }
     if (bad) atomicOr(&sm.flag, bad);
@@ -228,11 +250,16 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     // ---- is the row strictly increasing here?  Then every point is a vertex
     // (each edge's slope is its element; paper section 2.1).
     bool inc = L == 0 || base >= len || yp < yv[0];
+    if (full) {
 #pragma unroll
-    for (int b = 1; b < P; ++b)
-        if (base + b < len) inc = inc && yv[b - 1] < yv[b];
+        for (int b = 1; b < P; ++b) inc = inc && yv[b - 1] < yv[b];
+    } else {
+#pragma unroll
+        for (int b = 1; b < P; ++b)
+            if (base + b < len) inc = inc && yv[b - 1] < yv[b];
+    }
     const bool all = __syncthreads_and(inc) != 0;  // also publishes end_s, end_w
-    if (base + P > len) {
+    if (!full && base + P > len) {
         const double es = sm.end_s, ew = sm.end_w;
         if (base >= len) { s0 = es; w0 = ew; }
 #pragma unroll
@@ -245,14 +272,20 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     // k-1) is below the slope out of it (element k).  Points next to a padding
     // element are kept; padding points that are not thread ends are dropped.
     uint32_t cand = 1u | (1u << P);
+    if (full) {
 #pragma unroll
-    for (int k = 1; k < P; ++k) {
-        const int pidx = base + k;
-        bool c;
-        if (pidx > len) c = false;
-        else if (pidx < len) c = yv[k - 1] < yv[k];
-        else c = true;
-        if (c) cand |= 1u << k;
+        for (int k = 1; k < P; ++k)
+            if (yv[k - 1] < yv[k]) cand |= 1u << k;
+    } else {
+#pragma unroll
+        for (int k = 1; k < P; ++k) {
+            const int pidx = base + k;
+            bool c;
+            if (pidx > len) c = false;
+            else if (pidx < len) c = yv[k - 1] < yv[k];
+            else c = true;
+            if (c) cand |= 1u << k;
+        }
     }
 
     auto ent = [&](int i) -> Pt {
@@ -283,10 +316,16 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             pS[sk(base + b + 1)] = ps[b];
             if (WT) pW[sk(base + b + 1)] = pw[b];
         }
+        // live points: candidates below point len
         uint32_t alive = 0;
+        if (full) {
+            alive = (cand >> 1) & ((1u << P) - 1u);
+            if (L == NT - 1) alive &= ~(1u << (P - 1));
+        } else {
 #pragma unroll
-        for (int b = 0; b < P; ++b)
-            if (((cand >> (b + 1)) & 1u) && base + b + 1 < len) alive |= 1u << b;
+            for (int b = 0; b < P; ++b)
+                if (((cand >> (b + 1)) & 1u) && base + b + 1 < len) alive |= 1u << b;
+        }
         if (L == 0) {
             sm.qk[0][0] = 0;
             sm.qS[0][0] = 0.0;
@@ -741,11 +780,13 @@ __device__ __forceinline__ void chunk_hull(const float* __restrict__ y, const fl
             if (L == NT - 1) cw[NT] = pw[P - 1];
         }
         if (L == 0) wr->v[0] = make_double2(0.0, 0.0);
+        if (base + 1 < kWinK || base + P >= h - kWinK || h <= 2 * kWinK) {  // threads with window points
 #pragma unroll
-        for (int b = 0; b < P; ++b) {
-            const int k = base + b + 1;
-            const int e = k <= len ? wslot(k) : -1;
-            if (e >= 0) wr->v[e] = make_double2(ps[b], WT ? pw[b] : (double)k);
+            for (int b = 0; b < P; ++b) {
+                const int k = base + b + 1;
+                const int e = k <= len ? wslot(k) : -1;
+                if (e >= 0) wr->v[e] = make_double2(ps[b], WT ? pw[b] : (double)k);
+            }
         }
         cflag |= kChunkInc;
     } else if (MODE == kHullQuick && (ho.all || ho.fail)) {
