@@ -357,23 +357,19 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 int bk = 0;
                 if (lv == 0) {
                     // one chord, from point 0 to point len: the thread's own
-                    // points, from registers
+                    // points, from registers, without branches (with A at
+                    // the origin the depth is cross3(A, P, B) term for term)
+                    unsigned long long best = 0ull;
 #pragma unroll
                     for (int b = 0; b < P; ++b) {
-                        if ((alive >> b) & 1u) {
-                            const int k = base + b + 1;
-                            const Pt Pk{WT ? pw[b] : (double)k, ps[b]};
-                            const double c = cross3(A, Pk, B);
-                            if (c > 0.0) {
-                                if (c > bc) {
-                                    bc = c;
-                                    bk = k;
-                                }
-                            } else {
-                                alive &= ~(1u << b);
-                            }
-                        }
+                        const int k = base + b + 1;
+                        const double c = __dmul_rn(WT ? pw[b] : (double)k, B.s) - __dmul_rn(ps[b], B.w);
+                        const bool live = ((alive >> b) & 1u) && c > 0.0;
+                        if (!live) alive &= ~(1u << b);
+                        const unsigned long long key = live ? mkkey(c, k) : 0ull;
+                        best = key > best ? key : best;
                     }
+                    qbest = best;
                 } else {
                     // chord i runs from A to B (index nk); the next chords come
                     // from the list when this thread's points pass a vertex
@@ -407,8 +403,8 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                         }
                     }
                     qi = i;
+                    qbest = bk ? mkkey(bc, bk) : 0ull;
                 }
-                qbest = bk ? mkkey(bc, bk) : 0ull;
             }
             if (qbest) atomicMax(&qkey[qi], qbest);
             __syncthreads();
