@@ -896,8 +896,11 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     const bool vec = ((((uintptr_t)go) | (uintptr_t)gb) & 15u) == 0;
     auto store4 = [&](int e, float4 v, int4 b) {
         if (vec && e + 4 <= len) {
-            *reinterpret_cast<float4*>(go + e) = v;
-            if (gb) *reinterpret_cast<int4*>(gb + e) = b;
+            // streaming stores: the output is not read again here
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            typedef int i4v __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(f4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f4v*>(go + e));
+            if (gb) __builtin_nontemporal_store(i4v{b.x, b.y, b.z, b.w}, reinterpret_cast<i4v*>(gb + e));
         } else {
             const float vv[4] = {v.x, v.y, v.z, v.w};
             const int bb[4] = {b.x, b.y, b.z, b.w};
@@ -967,7 +970,9 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
             if (vy && e0 + 4 <= len) {
-                ya[g] = *reinterpret_cast<const float4*>(gy + e0);
+                typedef float f4v __attribute__((ext_vector_type(4)));
+                const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gy + e0));
+                ya[g] = make_float4(t.x, t.y, t.z, t.w);
             } else {
                 ya[g].x = e0 < len ? gy[e0] : 0.0f;
                 ya[g].y = e0 + 1 < len ? gy[e0 + 1] : 0.0f;
