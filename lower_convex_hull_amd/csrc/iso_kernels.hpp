@@ -78,7 +78,7 @@ struct GroupWin {
     int32_t h;
     int32_t nseg;
     int32_t flags;  // the group's data flags (kFlagData bits of its chunks)
-    int32_t pad;
+    int32_t pre1;   // vertices in the first segment of the group's list
     double2 v[2 * kGWinK];
     int32_t tag[2 * kGWinK];
 };

@@ -503,6 +503,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     if (tid == 0) {
         gwo->h = hg;
         gwo->nseg = nseg;
+        gwo->pre1 = pre[1];
     }
     if (wid == 0) {
         // the group's data flags, for the second stage
@@ -762,7 +763,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             const int4 d = D[t];
             // a whole group list (always so where every merge was convex)
             // needs no search
-            s_ilo[t] = d.y == 0 ? 0 : (d.y == 1 ? (ws.gpre[rb + d.x * G + 1] > 1 ? 0 : 1) : seg_of(d.x, d.y));
+            s_ilo[t] = d.y == 0 ? 0 : (d.y == 1 ? (GW[d.x].pre1 > 1 ? 0 : 1) : seg_of(d.x, d.y));
             s_ihi[t] = d.z == GH[d.x] - 1 ? s_gn[d.x] - 1 : seg_of(d.x, d.z);
         }
         __syncthreads();
