@@ -1,6 +1,11 @@
-"""Builds libiso.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc."""
+"""Builds libiso.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+
+Each source is compiled to an object of its own, in parallel, and the objects
+are linked into lower_convex_hull_amd/libiso.so.
+"""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -8,22 +13,37 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libiso.so")
 SOURCES = ["iso_api.hip", "iso_kernels.hip", "iso_merge.hip", "iso_copy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    tmp = f"{obj}.tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, "-c", "-o", tmp, os.path.join(CSRC, src)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, obj)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    os.makedirs(OBJ, exist_ok=True)
+    workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = f"{LIB}.tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

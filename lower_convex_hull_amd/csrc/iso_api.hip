@@ -27,7 +27,7 @@ struct Plan {
     size_t off_chunk_flag = 0, off_tot_S = 0, off_tot_W = 0, off_hull_cnt = 0;
     size_t off_slot_idx = 0, off_slot_S = 0, off_slot_W = 0, off_st_S = 0, off_st_W = 0, off_win = 0;
     size_t off_desc = 0, off_node_cnt = 0, off_vb = 0, off_rec = 0, off_desc_scr = 0, off_mi = 0;
-    size_t off_gwin = 0, off_gtot = 0, off_cst = 0, off_gpre = 0, off_root_n = 0, off_ck_S = 0, off_ck_W = 0, off_redo_n = 0, off_rslope = 0;
+    size_t off_gwin = 0, off_gtot = 0, off_cst = 0, off_gpre = 0, off_root_n = 0, off_ck_S = 0, off_ck_W = 0, off_rslope = 0;
     size_t off_cp_a = 0, off_cp_b = 0, off_cp_off = 0, off_cp_cnt = 0, off_cp_off2 = 0,
            off_cp_cnt2 = 0, off_cp_cut = 0, off_cp_cut2 = 0;
 };
@@ -79,7 +79,6 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
     p->off_cst = take(M * sizeof(double2));
     p->off_gpre = take(M * sizeof(int32_t));
     p->off_root_n = take(R * sizeof(int32_t));
-    p->off_redo_n = take(sizeof(int32_t));
     p->off_rslope = take(M * sizeof(double));
     p->off_ck_S = take(M * (iso::kLongNT + 1) * sizeof(double));
     p->off_ck_W = weighted ? take(M * (iso::kLongNT + 1) * sizeof(double)) : 0;
@@ -125,7 +124,6 @@ iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control)
     ws.cst = at<double2>(base, p.off_cst);
     ws.gpre = at<int32_t>(base, p.off_gpre);
     ws.root_n = at<int32_t>(base, p.off_root_n);
-    ws.redo_n = at<int32_t>(base, p.off_redo_n);
     ws.rslope = at<double>(base, p.off_rslope);
     ws.ck_S = at<double>(base, p.off_ck_S);
     ws.ck_W = weighted ? at<double>(base, p.off_ck_W) : nullptr;

@@ -726,15 +726,6 @@ __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r
 // entries k*E .. k*E+cnt[k]-1; at level l (span 2^l) node a and node a+span
 // merge into node a, one wave per merge.  Leaves the root's hull in entries
 // 0..cnt[0]-1.  There is no workgroup barrier between levels: node a's merges
-// at every level belong to one wave (merge_owner), which records in ver[a]
-// (LDS, zeroed by the caller before its last barrier) how many levels node a
-// has been through; a merge waits only until its right node has been through
-// every level at which that node had a partner.  A wait is only ever for a
-// lower level, so every wait ends.
-// Merges the nodes of a compact-array tree: node k of the first level is
-// entries k*E .. k*E+cnt[k]-1; at level l (span 2^l) node a and node a+span
-// merge into node a, one wave per merge.  Leaves the root's hull in entries
-// 0..cnt[0]-1.  There is no workgroup barrier between levels: node a's merges
 // at every level belong to one wave, which records in ver[a] (LDS, zeroed by
 // the caller before its last barrier) how many levels node a has been
 // through; a merge waits only until its right node has been through every

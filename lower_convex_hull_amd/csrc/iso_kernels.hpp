@@ -21,7 +21,6 @@ constexpr int kRedoGrid = 768;      // workgroups of the fallback chunk kernel (
 constexpr int kExpTile = 512;       // surviving vertices of a chunk the expansion keeps in LDS
 constexpr int kExpNT = 128;        // threads of an expansion workgroup (one chunk, 32 elements each)
 constexpr int kMergeNT = 1024;
-constexpr int kMergeLdsMax = 3072;  // rows with more chunks keep their lists in the workspace
 constexpr int kWinK = 16;           // hull vertices kept at each end of a chunk's window
 constexpr int kGWinK = 32;          // the same for a group hull's window
 constexpr int kGroup = 64;          // chunks per group of the first merge stage
@@ -41,7 +40,8 @@ constexpr int kFlagData = kFlagNonfinite | kFlagWeight;
 // hull vertex (position = point index) and the chunk's slot is not written;
 // its points are recomputed from the input and the per-thread checkpoints.
 constexpr int kChunkInc = 4;
-// Chunk flag: the first chunk kernel left this chunk to the second.
+// Chunk flag: the chunk kernel gave up on this chunk's hull (its window header
+// then holds h = 0); the first merge stage or the fallback kernel rebuilds it.
 constexpr int kChunkRedo = 8;
 
 // Reconstruction record of one chunk, written by the merge phase.
@@ -108,7 +108,6 @@ struct LongWs {
     double2* cst;         // [R*m] chunk starts relative to their group's start
     int32_t* gpre;        // [R*m] vertices before each segment of a group's list
     int32_t* root_n;      // [R] segments in the root list (desc_scr) of each row
-    int32_t* redo_n;      // [1] chunks the first chunk kernel left over (reset by the expansion)
     double* rslope;       // [R*m] slope of the root edge into each root segment (from the previous one)
     double* ck_S;         // [R*m*(kLongNT+1)] S at each thread's first point (and the chunk end)
     double* ck_W;         // (weighted only)
@@ -161,6 +160,10 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
 // The merge phase of the vertex-copying control (iso_copy.hip); leaves the
 // reconstruction records in ws.rec like the segment-list merge.
 hipError_t launch_copy_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
+
+// Whether rows of m chunks take the two-stage merge (k_group_merge, then
+// k_top_merge when there is more than one group).
+inline bool two_stage_merge(int m) { return (m + kGroup - 1) / kGroup <= kTopMax; }
 
 hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
                        float* out, int32_t* block_id, bool copy_control, hipStream_t st);

@@ -5,21 +5,23 @@
 // (section 3.4, Corollary 4.5).
 #include "iso_kernels.hpp"
 
+#include <mutex>
+
 #include "iso_device.hpp"
+#include "iso_hull.hpp"
 
 namespace iso {
 namespace {
 
-// One workgroup per row runs every level of the merge tree.  Segment lists
-// live in LDS when the row has at most kMergeLdsMax chunks (else in the
-// workspace).  Per level: one thread per merge finds its bridge and cuts the two
-// boundary segments in place; then teams of threads move each right list's
-// remaining descriptors down behind the left list's (through a scratch copy,
-// since the two ranges may overlap).
-template <bool WT, bool INLDS>
+// Rows beyond the two-stage merge: one workgroup per row runs every level of
+// the merge tree with the segment lists in the workspace.  Per level: one
+// thread per merge finds its bridge and cuts the two boundary segments in
+// place; then teams of threads move each right list's remaining descriptors
+// down behind the left list's (through a scratch copy, since the two ranges
+// may overlap).
+template <bool WT>
 __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     constexpr int NT = kMergeNT;
-    extern __shared__ uint2 dyn_lds[];
     __shared__ double red[NT / 64 + 1];
     __shared__ int ired[NT / 64 + 1];
     __shared__ int sflag;
@@ -31,30 +33,13 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     const int tid = threadIdx.x;
     const int wid = tid >> 6, wlane = tid & 63;
 
-    uint2* D;
-    uint2* SCR;
-    int32_t* CNT;
-    int2* MI;
-    int32_t* HC;
-    double* STS;
-    double* STW;
-    if (INLDS) {
-        D = dyn_lds;
-        SCR = D + m;
-        MI = reinterpret_cast<int2*>(SCR + m);
-        STS = reinterpret_cast<double*>(MI + (m / 2 + 1));
-        STW = STS + m;  // used when weighted
-        CNT = reinterpret_cast<int32_t*>(STW + (WT ? m : 0));
-        HC = CNT + m;
-    } else {
-        D = ws.desc + rb;
-        SCR = ws.desc_scr + rb;
-        CNT = ws.node_cnt + rb;
-        MI = ws.merge_info + rb;
-        HC = ws.hull_cnt + rb;
-        STS = ws.st_S + rb;
-        STW = WT ? ws.st_W + rb : nullptr;
-    }
+    uint2* const D = ws.desc + rb;
+    uint2* const SCR = ws.desc_scr + rb;
+    int32_t* const CNT = ws.node_cnt + rb;
+    int2* const MI = ws.merge_info + rb;
+    int32_t* const HC = ws.hull_cnt + rb;
+    double* const STS = ws.st_S + rb;
+    double* const STW = WT ? ws.st_W + rb : nullptr;
 
     // ---- row flags, chunk starts (exclusive scan of the chunk totals)
     if (tid == 0) sflag = 0;
@@ -78,8 +63,7 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
         }
     }
     for (int j = tid; j < m; j += NT) {
-        const int h = ws.hull_cnt[rb + j];
-        if (INLDS) HC[j] = h;
+        const int h = HC[j];
         D[j] = mkdesc(j, 0, h - 1);
         CNT[j] = 1;
     }
@@ -308,10 +292,13 @@ template <bool WT>
 __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
     constexpr int NT = kGroupNT, G = kGroup, E = 2 * kWinK, EG = 2 * kGWinK;
     static_assert(G == 64, "one wave numbers a group's segments");
-    // the generic path's chunk windows, or the fast path's compact arrays
+    // the generic path's chunk windows, or the fast path's compact arrays, or
+    // (before either) the rebuild of a chunk hull the chunk kernel gave up on
+    using RedoSmem = HullSmem<NT, kChunk / NT, WT, kHullChains>;
     constexpr size_t kGen = sizeof(WinRec) * G;
     constexpr size_t kFast = (size_t)G * E * (8 + 8 + 4);
-    __shared__ __align__(16) unsigned char pool[kGen > kFast ? kGen : kFast];
+    constexpr size_t kPool0 = kGen > kFast ? kGen : kFast;
+    __shared__ __align__(16) unsigned char pool[kPool0 > sizeof(RedoSmem) ? kPool0 : sizeof(RedoSmem)];
     __shared__ double lS[G], lW[G];
     __shared__ int32_t HC[G], CNT[G], VER[G], pre[G + 1];
     __shared__ uint2 D[G], SCR[G];
@@ -346,7 +333,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         if (WT) tw = ws.tot_W[rb + j0 + wlane];
     }
     // hull counts; the fast path needs every chunk hull whole in its window
-    bool ok = true;
+    bool ok = true, redo = false;
 #pragma unroll
     for (int q = 0; q < kRaw; ++q) {
         const int i = tid + q * NT;
@@ -354,6 +341,30 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             const int h = (int)(uint32_t)__double_as_longlong(raw[q].x);  // WinRec::h
             HC[i / kW2] = h;
             ok = ok && h <= E;
+            redo = redo || h == 0;
+        }
+    }
+    if (__syncthreads_or(redo)) {
+        // chunks the chunk kernel gave up on (header h = 0, written in this
+        // call): the whole workgroup rebuilds each with chains and merges,
+        // then every window word is read again
+        RedoSmem& hs = *reinterpret_cast<RedoSmem*>(pool);
+        for (int i = 0; i < gc; ++i) {
+            if (HC[i] != 0) continue;  // the same in every thread
+            chunk_hull<NT, kChunk / NT, kHullChains, WT>(ws.y, ws.w, ws.n, m, ws.sign, ws, 0, hs,
+                                                         rb + j0 + i);
+            __syncthreads();
+        }
+        ok = true;
+#pragma unroll
+        for (int q = 0; q < kRaw; ++q) {
+            const int i = tid + q * NT;
+            raw[q] = i < nraw ? wsrc[i] : make_double2(0.0, 0.0);
+            if (i < nraw && i % kW2 == 0) {
+                const int h = (int)(uint32_t)__double_as_longlong(raw[q].x);
+                HC[i / kW2] = h;
+                ok = ok && h <= E;
+            }
         }
     }
     if (wid == 0) {
@@ -862,20 +873,13 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
 
 }  // namespace
 
-size_t merge_lds_bytes(int m, bool weighted) {
-    // D, SCR (8 B each), MI (8 B per merge), STS (8 B), STW (8 B, weighted),
-    // CNT, HC (4 B each)
-    return (size_t)m * 16 + (size_t)(m / 2 + 1) * 8 + (size_t)m * (weighted ? 16 : 8) +
-           (size_t)m * 8;
-}
-
 // The merge phase over segment lists: one workgroup per row, lists in LDS when
 // they fit.
 hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
     const bool wt = sh.weighted;
     const int ng = (sh.m + kGroup - 1) / kGroup;
     const unsigned R = (unsigned)sh.rows;
-    if (ng <= kTopMax) {
+    if (two_stage_merge(sh.m)) {
         *rec_done = false;
         timed_begin(kPhaseMerge, st);
         if (wt)
@@ -887,15 +891,14 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
         timed_end(st);
         if (ng > 1) {
             const size_t lds = top_lds_bytes(ng, sh.m);
-            static bool attr_set = false;
-            if (!attr_set) {
+            static std::once_flag attr_once;
+            std::call_once(attr_once, [] {
                 const int maxb = (int)top_lds_bytes(kTopMax, kTopMax * kGroup);
                 (void)hipFuncSetAttribute((const void*)k_top_merge<true>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
                 (void)hipFuncSetAttribute((const void*)k_top_merge<false>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-                attr_set = true;
-            }
+            });
             timed_begin(kPhaseMergeTop, st);
             if (wt)
                 hipLaunchKernelGGL(k_top_merge<true>, dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
@@ -910,9 +913,9 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     *rec_done = true;
     timed_begin(kPhaseMerge, st);
     if (wt)
-        hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL(k_merge_rows<true>, dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     else
-        hipLaunchKernelGGL((k_merge_rows<false, false>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL(k_merge_rows<false>, dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     timed_end(st);
     return hipGetLastError();
 }

@@ -123,23 +123,27 @@ def test_c4_row1e7_dense(torch):
 
 
 def test_c5_calibration_rows(torch):
-    # 16 of the 256 rows at full length (2^20), same recipe; the full batch runs
-    # in test_c5_full_batch_sampled.
+    # 16 of the 256 rows at full length (2^20), same recipe; every row of the
+    # full batch is compared in test_c5_full_batch_every_row.
     y, w = inputs.config("c5_calib256x2p20", rows=16)
     check(torch, y, w, name="c5x16")
 
 
-def test_c5_full_batch_sampled(torch):
+def test_c5_full_batch_every_row(torch):
+    """The whole 256 x 2^20 calibration batch in one call, every row compared
+    with the oracle element by element (values and block ids)."""
     y, w = inputs.config("c5_calib256x2p20")
-    say("[parity] c5 full batch 256 x 2^20 (oracle on 24 sampled rows)")
-    st, out, bid = gpu_fit(torch, y, w, block_ids=False)
+    say("[parity] c5 full batch 256 x 2^20, every row against the oracle")
+    st, out, bid = gpu_fit(torch, y, w, block_ids=True)
     assert st == 0
-    rows = np.random.default_rng(0).choice(y.shape[0], 24, replace=False)
-    _, z64, _ = oracle.fit_rows_f32(y[rows], w[rows])
-    ok, wa, wo, r = fitcheck.parity(y[rows], w[rows], out[rows], z64)
-    assert ok, (wa, wo, rows[r])
-    # every row: the output is within [min y, max y] and its KKT total is ~0
-    assert np.all(out >= 0) and np.all(out <= 1)
+    for r0 in range(0, y.shape[0], 32):
+        sl = slice(r0, r0 + 32)
+        _, z64, obid = oracle.fit_rows_f32(y[sl], w[sl])
+        ok, wa, wo, r = fitcheck.parity(y[sl], w[sl], out[sl], z64)
+        assert ok, (wa, wo, r0 + r)
+        for r in range(z64.shape[0]):
+            assert fitcheck.block_ids_consistent(obid[r], bid[r0 + r], z64[r], y[r0 + r]), \
+                f"c5 block ids row {r0 + r}"
 
 
 # --------------------------------------------------------------------------- families, sizes, edges
@@ -338,6 +342,58 @@ def test_nonfinite_and_bad_weight_in_a_later_group(torch):
     w[1, 290_000] = 0.0
     st, _, _ = gpu_fit(torch, y2, w)
     assert st == iso.ISO_ERR_WEIGHT
+
+
+def _one_fallback_chunk_rows(rows, n, chunk, seed):
+    """Noisy rows in which one chunk of row 0 is strictly increasing but for one
+    repeated value: that chunk's hull keeps about 4096 vertices, so the chunk
+    kernel gives up on it and it is rebuilt (by the first merge stage, or by
+    the fallback kernel for rows beyond the two-stage merge)."""
+    y, _ = inputs.noisy(rows, n, seed)
+    c = iso.iso_chunk_size(n)
+    a, b = chunk * c, min(n, (chunk + 1) * c)
+    d, _ = inputs.dense(b - a, seed + 1)
+    seg = 1.0 + d[0]
+    seg[(b - a) // 2] = seg[(b - a) // 2 - 1]  # one tie: not strictly increasing
+    y[0, a:b] = seg
+    return y
+
+
+def test_workspace_contents_need_no_initialisation(torch):
+    """A workspace full of 0xFF bytes, then reused across shapes with its
+    previous call's contents left in it: rows where exactly one chunk is
+    rebuilt still match the oracle (the rebuild depends only on what the chunk
+    kernel wrote in the same call)."""
+    cases = [(1, 300_000, 17), (3, 150_000, 5), (2, 2 * 4096 + 77, 1), (1, 96 * 64 * 4096 + 5, 3000)]
+    nbytes = max(iso.iso_workspace_bytes(r, n, 0) for r, n, _ in cases)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    for rows, n, chunk in cases + cases[:2]:
+        y = _one_fallback_chunk_rows(rows, n, chunk, 40 + rows)
+        say(f"[parity] stale workspace rows={rows} n={n} fallback chunk {chunk}")
+        yt = torch.from_numpy(y).cuda()
+        out = torch.empty_like(yt)
+        bid = torch.empty(yt.shape, dtype=torch.int32, device="cuda")
+        st = iso.iso_fit_ex(yt.data_ptr(), None, rows, n, out.data_ptr(), bid.data_ptr(),
+                            ws.data_ptr(), nbytes, iso._stream_handle(None), 0)
+        torch.cuda.synchronize()
+        assert st == iso.ISO_OK, iso.iso_status_str(st)
+        o = out.cpu().numpy()
+        _, z64, obid = oracle.fit_rows_f32(y)
+        ok, wa, wo, r = fitcheck.parity(y, None, o, z64)
+        assert ok, (rows, n, wa, wo, r)
+        b = bid.cpu().numpy()
+        for r in range(rows):
+            assert fitcheck.block_ids_consistent(obid[r], b[r], z64[r], y[r]), (rows, n, r)
+        del yt, out, bid
+    # the blocking entry point's cached workspace, reused across two shapes
+    for rows, n, chunk in ((1, 300_000, 40), (4, 100_000, 3)):
+        y = _one_fallback_chunk_rows(rows, n, chunk, 60 + rows)
+        yt = torch.from_numpy(y).cuda()
+        out = torch.empty_like(yt)
+        assert iso.iso_fit(yt.data_ptr(), None, rows, n, out.data_ptr()) == iso.ISO_OK
+        _, z64, _ = oracle.fit_rows_f32(y)
+        assert fitcheck.parity(y, None, out.cpu().numpy(), z64)[0], (rows, n)
+    iso.iso_release()
 
 
 def test_deterministic(torch):
