@@ -43,7 +43,9 @@
  *   ISO_ERR_NOMEM        iso_fit could not allocate its cached workspace.
  *   ISO_ERR_HIP          a HIP runtime call or kernel launch failed.
  *   ISO_ERR_WORKSPACE    iso_fit_ex got a workspace smaller than
- *                        iso_workspace_bytes() asks for.  Nothing launched.
+ *                        iso_workspace_bytes() asks for, or the shape needs
+ *                        more than iso_fit_noalloc's ISO_NOALLOC_BYTES.
+ *                        Nothing launched.
  *   rows == 0 or n == 0 is a no-op that returns ISO_OK.
  *
  * The two warning/error statuses that depend on the data (NONFINITE, WEIGHT)
@@ -115,6 +117,26 @@ int iso_fit(const float* y, const float* w, int64_t rows, int64_t n, float* out)
 int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* out,
                int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
                uint32_t flags);
+
+/*
+ * iso_fit_noalloc - iso_fit_ex without a caller workspace and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *   y, w, out, block_id, stream, flags as for iso_fit_ex.
+ * The workspace is a fixed device array of ISO_NOALLOC_BYTES that the library
+ * holds on every device it runs on until the process ends; shapes whose
+ * iso_workspace_bytes exceeds it return ISO_ERR_WORKSPACE with nothing
+ * launched.  The call never calls hipMalloc, hipFree or any other allocating
+ * routine (host or device); its first call on a device looks up the array's
+ * device address once.  Every call on one device shares that array and leaves
+ * its contents in it (the kernels need no initialised workspace), so calls on
+ * one device must not overlap in time: overlapping calls race on it.  Without
+ * ISO_F_NOCHECK the call synchronises with `stream` (not capturable then);
+ * with it the call only enqueues work.
+ */
+#define ISO_NOALLOC_BYTES (64u << 20)
+int iso_fit_noalloc(const float* y, const float* w, int64_t rows, int64_t n, float* out,
+                    int32_t* block_id, void* stream, uint32_t flags);
 
 /* Bytes of device workspace iso_fit_ex needs for this shape and these flags
  * (weighted or not is part of the shape: pass ISO_F_WEIGHTED_HINT in flags

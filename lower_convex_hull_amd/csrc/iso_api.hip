@@ -23,6 +23,7 @@ struct Plan {
     int m = 0;
     size_t bytes = 0;
     size_t off_row_flag = 0;
+    size_t off_flag_all = 0;  // one int: the OR of the row flags, for the check
     // long rows
     size_t off_chunk_flag = 0, off_tot_S = 0, off_tot_W = 0, off_hull_cnt = 0;
     size_t off_slot_idx = 0, off_slot_S = 0, off_slot_W = 0, off_st_S = 0, off_st_W = 0, off_win = 0;
@@ -46,6 +47,7 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
     };
     const size_t R = (size_t)rows;
     p->off_row_flag = take(R * sizeof(int32_t));
+    p->off_flag_all = take(sizeof(int32_t));
     if (n <= iso::kShortMax) {
         if (rows > 0x7fffffffLL) return false;
         p->bytes = at;
@@ -178,6 +180,84 @@ Cache& cache() {
     return c;
 }
 
+// The fit on `stream` with `workspace`: argument checks, launches, and (without
+// ISO_F_NOCHECK) the data check.  Allocates nothing, on the device or the host.
+int fit_body(const float* y, const float* w, int64_t rows, int64_t n, float* out,
+             int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
+             uint32_t flags) {
+    if (!y || !out || rows < 0 || n < 0 || (flags & ~kKnownFlags)) return ISO_ERR_ARG;
+    if (rows == 0 || n == 0) return ISO_OK;
+    const bool weighted = w != nullptr;
+    const bool copy_control = (flags & ISO_F_COPY_CONTROL) != 0;
+    Plan p;
+    if (!plan(rows, n, weighted, copy_control, &p)) return ISO_ERR_ARG;
+    const size_t nb = (size_t)rows * (size_t)n * sizeof(float);
+    if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, nb, y, nb) ||
+        overlaps(block_id, nb, w, nb) || overlaps(block_id, nb, out, nb))
+        return ISO_ERR_ARG;
+    if (((uintptr_t)y | (uintptr_t)out | (uintptr_t)w | (uintptr_t)block_id) & 3u) return ISO_ERR_ARG;
+    if (!workspace || workspace_bytes < p.bytes) return ISO_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % kAlign) return ISO_ERR_ARG;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const float sign = (flags & ISO_F_DECREASING) ? -1.0f : 1.0f;
+    int32_t* row_flag = at<int32_t>(workspace, p.off_row_flag);
+    hipError_t e;
+    if (!p.long_rows) {
+        e = iso::launch_short(y, w, rows, n, sign, out, block_id, row_flag, st);
+    } else {
+        iso::LongShape sh{rows, n, p.m, weighted, sign};
+        iso::LongWs ws = long_ws(workspace, p, weighted, copy_control);
+        e = iso::launch_long(y, w, sh, ws, out, block_id, copy_control, st);
+    }
+    if (e != hipSuccess) return ISO_ERR_HIP;
+    if (flags & ISO_F_NOCHECK) return ISO_OK;
+
+    int32_t* all = at<int32_t>(workspace, p.off_flag_all);
+    if (iso::launch_flags_or(row_flag, rows, all, st) != hipSuccess) return ISO_ERR_HIP;
+    int32_t any = 0;
+    if (hipMemcpyAsync(&any, all, sizeof(any), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return ISO_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return ISO_ERR_HIP;
+    if (any & iso::kFlagWeight) return ISO_ERR_WEIGHT;
+    if (any & iso::kFlagNonfinite) return ISO_WARN_NONFINITE;
+    return ISO_OK;
+}
+
+}  // namespace
+
+// The no-alloc entry point's workspace: a device array of ISO_NOALLOC_BYTES
+// that every GPU the library runs on holds until the process ends.  Its name
+// is not a device address in host code: the address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[ISO_NOALLOC_BYTES];
+
+namespace {
+
+struct ScratchTable {
+    std::mutex mu;
+    void* ptr[64] = {};
+};
+ScratchTable& scratch_table() {
+    static ScratchTable t;
+    return t;
+}
+
+// Device address of `scratch` on the current device (set up on the first call
+// on each device), or nullptr on a HIP error.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    ScratchTable& t = scratch_table();
+    std::lock_guard<std::mutex> lock(t.mu);
+    if (!t.ptr[dev]) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        t.ptr[dev] = q;
+    }
+    return t.ptr[dev];
+}
+
 }  // namespace
 
 namespace iso {
@@ -268,44 +348,19 @@ size_t iso_workspace_bytes(int64_t rows, int64_t n, uint32_t flags) {
 int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* out,
                int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
                uint32_t flags) {
+    return fit_body(y, w, rows, n, out, block_id, workspace, workspace_bytes, stream, flags);
+}
+
+int iso_fit_noalloc(const float* y, const float* w, int64_t rows, int64_t n, float* out,
+                    int32_t* block_id, void* stream, uint32_t flags) {
     if (!y || !out || rows < 0 || n < 0 || (flags & ~kKnownFlags)) return ISO_ERR_ARG;
     if (rows == 0 || n == 0) return ISO_OK;
-    const bool weighted = w != nullptr;
-    const bool copy_control = (flags & ISO_F_COPY_CONTROL) != 0;
     Plan p;
-    if (!plan(rows, n, weighted, copy_control, &p)) return ISO_ERR_ARG;
-    const size_t nb = (size_t)rows * (size_t)n * sizeof(float);
-    if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, nb, y, nb) ||
-        overlaps(block_id, nb, w, nb) || overlaps(block_id, nb, out, nb))
-        return ISO_ERR_ARG;
-    if (((uintptr_t)y | (uintptr_t)out | (uintptr_t)w | (uintptr_t)block_id) & 3u) return ISO_ERR_ARG;
-    if (!workspace || workspace_bytes < p.bytes) return ISO_ERR_WORKSPACE;
-    if ((uintptr_t)workspace % kAlign) return ISO_ERR_ARG;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const float sign = (flags & ISO_F_DECREASING) ? -1.0f : 1.0f;
-    int32_t* row_flag = at<int32_t>(workspace, p.off_row_flag);
-    hipError_t e;
-    if (!p.long_rows) {
-        e = iso::launch_short(y, w, rows, n, sign, out, block_id, row_flag, st);
-    } else {
-        iso::LongShape sh{rows, n, p.m, weighted, sign};
-        iso::LongWs ws = long_ws(workspace, p, weighted, copy_control);
-        e = iso::launch_long(y, w, sh, ws, out, block_id, copy_control, st);
-    }
-    if (e != hipSuccess) return ISO_ERR_HIP;
-    if (flags & ISO_F_NOCHECK) return ISO_OK;
-
-    std::vector<int32_t> hf((size_t)rows);
-    if (hipMemcpyAsync(hf.data(), row_flag, hf.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
-                       st) != hipSuccess)
-        return ISO_ERR_HIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return ISO_ERR_HIP;
-    int any = 0;
-    for (int32_t f : hf) any |= f;
-    if (any & iso::kFlagWeight) return ISO_ERR_WEIGHT;
-    if (any & iso::kFlagNonfinite) return ISO_WARN_NONFINITE;
-    return ISO_OK;
+    if (!plan(rows, n, w != nullptr, (flags & ISO_F_COPY_CONTROL) != 0, &p)) return ISO_ERR_ARG;
+    if (p.bytes > (size_t)ISO_NOALLOC_BYTES) return ISO_ERR_WORKSPACE;
+    void* ws = scratch_ptr();
+    if (!ws) return ISO_ERR_HIP;
+    return fit_body(y, w, rows, n, out, block_id, ws, (size_t)ISO_NOALLOC_BYTES, stream, flags);
 }
 
 int iso_fit(const float* y, const float* w, int64_t rows, int64_t n, float* out) {

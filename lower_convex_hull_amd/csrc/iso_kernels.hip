@@ -352,7 +352,30 @@ hipError_t launch_short_t(const float* y, const float* w, int64_t rows, int64_t 
     return hipGetLastError();
 }
 
+// One workgroup ORs every row's data flags into one int (read back by the
+// checking path, so that a check copies four bytes whatever the batch).
+__global__ __launch_bounds__(1024) void k_flags_or(const int32_t* __restrict__ f, int64_t rows,
+                                                   int32_t* __restrict__ dst) {
+    __shared__ int red[16];
+    int v = 0;
+    for (int64_t r = threadIdx.x; r < rows; r += 1024) v |= f[r];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v |= __shfl_xor(v, d);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int a = 0;
+        for (int k = 0; k < 16; ++k) a |= red[k];
+        *dst = a;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, hipStream_t st) {
+    hipLaunchKernelGGL(k_flags_or, dim3(1), dim3(1024), 0, st, row_flag, rows, dst);
+    return hipGetLastError();
+}
 
 hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                         float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {

@@ -151,6 +151,9 @@ void timed_end(hipStream_t st);
 hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
                         float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
 
+// ORs the rows' data flags into *dst (one int) on the device, for the check.
+hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, hipStream_t st);
+
 // The merge phase over segment lists (iso_merge.hip).  Leaves either the
 // reconstruction records in ws.rec (*rec_done = true) or each row's root list
 // in ws.desc_scr with its prefix counts, from which the expansion computes

@@ -32,8 +32,11 @@ ISO_F_WEIGHTED_HINT = 0x100
 ISO_PHASE_NAMES = ("short_rows", "chunk_hulls", "merge", "expand", "copy_bridge", "copy_move",
                    "merge_top", "chunk_redo")
 
-EXPORTS = ("iso_fit", "iso_fit_ex", "iso_workspace_bytes", "iso_status_str", "iso_release",
-           "iso_chunk_size", "iso_short_row_max", "iso_timing_enable", "iso_timing_read")
+ISO_NOALLOC_BYTES = 64 << 20
+
+EXPORTS = ("iso_fit", "iso_fit_ex", "iso_fit_noalloc", "iso_workspace_bytes", "iso_status_str",
+           "iso_release", "iso_chunk_size", "iso_short_row_max", "iso_timing_enable",
+           "iso_timing_read")
 
 _lib = None
 
@@ -55,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.iso_fit.restype = ctypes.c_int
         L.iso_fit_ex.argtypes = [p, p, i64, i64, p, p, p, sz, p, u32]
         L.iso_fit_ex.restype = ctypes.c_int
+        L.iso_fit_noalloc.argtypes = [p, p, i64, i64, p, p, p, u32]
+        L.iso_fit_noalloc.restype = ctypes.c_int
         L.iso_workspace_bytes.argtypes = [i64, i64, u32]
         L.iso_workspace_bytes.restype = sz
         L.iso_status_str.argtypes = [ctypes.c_int]
@@ -80,6 +85,10 @@ def iso_fit(y_ptr, w_ptr, rows, n, out_ptr) -> int:
 def iso_fit_ex(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes, stream, flags) -> int:
     return lib().iso_fit_ex(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes,
                             stream, flags)
+
+
+def iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags) -> int:
+    return lib().iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags)
 
 
 def iso_workspace_bytes(rows, n, flags=0) -> int:
