@@ -8,7 +8,9 @@ The oracle computes the weighted isotonic fit of equation (1) of the paper
 with pool adjacent violators in f64; see iso_oracle.c for the readings taken.
 Parity is pinned for every routine here (tests/test_oracle.py): brute force over
 contiguous partitions, KKT prefix conditions, worked examples printed on the
-pages, closed forms and a library routine.
+pages, closed forms and a library routine; the vector-Jacobian product (paper
+section 6, "Gradient") by finite differences of the fit in y and in w, closed
+forms and block sums.
 """
 from __future__ import annotations
 
@@ -58,6 +60,10 @@ def _lib(mutant: int = 0) -> ctypes.CDLL:
         lib.oracle_brute_force.restype = ctypes.c_double
         lib.oracle_hull_fit.argtypes = [p, p, i64, p]
         lib.oracle_hull_fit.restype = i64
+        lib.oracle_vjp_f64.argtypes = [p, p, p, p, i64, p, p]
+        lib.oracle_vjp_f64.restype = ctypes.c_int
+        lib.oracle_vjp_rows_f32.argtypes = [p, p, p, p, i64, i64, p, p]
+        lib.oracle_vjp_rows_f32.restype = ctypes.c_int
         _libs[mutant] = lib
     return _libs[mutant]
 
@@ -119,3 +125,39 @@ def hull_fit(y, w=None):
     if nv < 0:
         raise MemoryError("oracle: allocation failed")
     return z, int(nv)
+
+
+def vjp(y, w, g, block_id=None, mutant: int = 0):
+    """Vector-Jacobian product of one row's fit in f64: (d/dy, d/dw) for the
+    gradient g with respect to the fit, over block_id's blocks (None: the
+    oracle's own).  d/dw is None for unit weights."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    w = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
+    bid = None if block_id is None else np.ascontiguousarray(block_id, dtype=np.int32)
+    n = y.shape[0]
+    gy = np.empty(n, np.float64)
+    gw = np.empty(n, np.float64) if w is not None else None
+    if _lib(mutant).oracle_vjp_f64(_ptr(y), _ptr(w), _ptr(g), _ptr(bid), n, _ptr(gy), _ptr(gw)) != 0:
+        raise MemoryError("oracle: allocation failed")
+    return gy, gw
+
+
+def vjp_rows_f32(y, w, g, block_id=None, mutant: int = 0):
+    """Rows of f32 data and gradient -> f64 (d/dy, d/dw) of each row's fit over
+    block_id's blocks (None: the oracle's own); d/dw is None for unit weights."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    if y.ndim == 1:
+        y = y[None, :]
+    rows, n = y.shape
+    g = np.ascontiguousarray(g, dtype=np.float32).reshape(rows, n)
+    if w is not None:
+        w = np.ascontiguousarray(w, dtype=np.float32).reshape(rows, n)
+    bid = None if block_id is None else np.ascontiguousarray(block_id, dtype=np.int32).reshape(rows, n)
+    gy = np.empty((rows, n), np.float64)
+    gw = np.empty((rows, n), np.float64) if w is not None else None
+    rc = _lib(mutant).oracle_vjp_rows_f32(_ptr(y), _ptr(w), _ptr(g), _ptr(bid), rows, n, _ptr(gy),
+                                          _ptr(gw))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return gy, gw

@@ -37,9 +37,13 @@
  *    cumulative sum diagram (paper section 2.1, equations (2) and (3)), built
  *    with a monotone chain that drops points on or above a chord.
  *
- * Compile-time switch ORACLE_MUTANT=k (k >= 1) plants one deliberate mistake in
- * the PAVA routine.  It exists only so that the test suite can show that its
- * pins catch each planted mistake; the default build (no switch) has none.
+ * Also here: oracle_vjp_f64, the vector-Jacobian product of the fit (block
+ * averaging of the incoming gradient, paper section 6, "Gradient").
+ *
+ * Compile-time switch ORACLE_MUTANT=k (k >= 1) plants one deliberate mistake:
+ * k = 1..6 in the PAVA routine, k = 7..10 in the vector-Jacobian product.  It
+ * exists only so that the test suite can show that its pins catch each planted
+ * mistake; the default build (no switch) has none.
  */
 #include <math.h>
 #include <stdint.h>
@@ -252,4 +256,120 @@ int64_t oracle_hull_fit(const double* y, const double* w, int64_t n, double* z) 
     }
     free(W); free(S); free(h);
     return top;
+}
+
+/*
+ * Vector-Jacobian product of the fit (paper "Merge Hulls Without Copying
+ * Vertices: GPU Isotonic Regression", section 6, paragraph "Gradient").  The
+ * fit is constant on blocks, each block's value the weighted mean z of y over
+ * it, so its Jacobian averages over blocks.  With g the gradient with respect
+ * to the fit and, over an element's block, G the sum of g and W the sum of w:
+ *     d/dy_i = w_i G / W,        d/dw_i = (y_i - z) G / W,
+ * wherever the blocks do not change.
+ *   y[n], w[n] (NULL: unit weights), g[n]   f64.
+ *   block_id   the blocks to differentiate over (a block starts at element 0
+ *              and wherever the id changes), or NULL for this oracle's own
+ *              PAVA blocks.  A row whose first id is negative (a non-finite
+ *              row of the fit) gets NaN.
+ *   gy, gw     (either may be NULL) receive the gradients in f64.
+ * Every sum is formed left to right over the block in f64.
+ * Returns 0, or -1 when a scratch allocation fails.
+ */
+int oracle_vjp_f64(const double* y, const double* w, const double* g, const int32_t* block_id,
+                   int64_t n, double* gy, double* gw) {
+    if (n <= 0) return 0;
+    int32_t* own = NULL;
+    const int32_t* bid = block_id;
+    if (!bid) {
+        double* z = (double*)malloc((size_t)n * sizeof(double));
+        own = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+        if (!z || !own) {
+            free(z); free(own);
+            return -1;
+        }
+        if (oracle_pava_f64(y, w, n, z, own) < 0) {
+            free(z); free(own);
+            return -1;
+        }
+        free(z);
+        bid = own;
+    }
+    if (bid[0] < 0) {
+        for (int64_t i = 0; i < n; ++i) {
+            if (gy) gy[i] = NAN;
+            if (gw) gw[i] = NAN;
+        }
+        free(own);
+        return 0;
+    }
+    int64_t a = 0;
+    while (a < n) {
+        int64_t b = a + 1; /* the block is [a, b) */
+        while (b < n && bid[b] == bid[a]) ++b;
+#if ORACLE_MUTANT == 10 /* mistake: the block's sums run one element too far */
+        int64_t bs = b < n ? b + 1 : b;
+#else
+        int64_t bs = b;
+#endif
+        double G = 0.0, W = 0.0, S = 0.0;
+        for (int64_t i = a; i < bs; ++i) {
+            double wi = w ? w[i] : 1.0;
+            G += g[i];
+            W += wi;
+            S += wi * y[i];
+        }
+#if ORACLE_MUTANT == 9 /* mistake: G divided by the element count, not by W */
+        double r = G / (double)(bs - a);
+#else
+        double r = G / W;
+#endif
+        double z = S / W;
+        for (int64_t i = a; i < b; ++i) {
+            double wi = w ? w[i] : 1.0;
+#if ORACLE_MUTANT == 7 /* mistake: the weight factor of d/dy dropped */
+            if (gy) gy[i] = r;
+#else
+            if (gy) gy[i] = wi * r;
+#endif
+#if ORACLE_MUTANT == 8 /* mistake: d/dw with its sign reversed */
+            if (gw) gw[i] = (z - y[i]) * r;
+#else
+            if (gw) gw[i] = (y[i] - z) * r;
+#endif
+        }
+        a = b;
+    }
+    free(own);
+    return 0;
+}
+
+/*
+ * Rows of one common length, row-major, f32 inputs widened exactly to f64:
+ * the vector-Jacobian product of each row's fit (oracle_vjp_f64 per row).
+ *   w may be NULL (unit weights); block_id may be NULL (own blocks).
+ *   gy64, gw64 (either may be NULL) receive the f64 gradients.
+ * Returns 0, or -1 on allocation failure.
+ */
+int oracle_vjp_rows_f32(const float* y, const float* w, const float* g, const int32_t* block_id,
+                        int64_t rows, int64_t n, double* gy64, double* gw64) {
+    if (rows <= 0 || n <= 0) return 0;
+    double* yd = (double*)malloc((size_t)n * sizeof(double));
+    double* wd = w ? (double*)malloc((size_t)n * sizeof(double)) : NULL;
+    double* gd = (double*)malloc((size_t)n * sizeof(double));
+    if (!yd || !gd || (w && !wd)) {
+        free(yd); free(wd); free(gd);
+        return -1;
+    }
+    int rc = 0;
+    for (int64_t r = 0; r < rows && rc == 0; ++r) {
+        for (int64_t i = 0; i < n; ++i) {
+            yd[i] = (double)y[r * n + i];
+            gd[i] = (double)g[r * n + i];
+            if (w) wd[i] = (double)w[r * n + i];
+        }
+        rc = oracle_vjp_f64(yd, wd, gd, block_id ? block_id + r * n : NULL, n,
+                            gy64 ? gy64 + r * n : NULL, gw64 ? gw64 + r * n : NULL);
+    }
+    free(yd); free(wd); free(gd);
+    return rc;
 }

@@ -265,3 +265,148 @@ def test_planted_mistakes_are_caught(mutant):
         if pin_brute_force(mutant=mutant, count=200):
             caught.append("pin_brute_force")
     assert caught, f"mutant {mutant} passed every pin"
+
+
+# ----------------------------------------------------------------------------- VJP pins
+# The vector-Jacobian product of the fit (paper section 6, "Gradient"; the
+# paper's appendix C checks it against finite differences in y and in w in
+# float64 and against block sums).
+
+VJP_MUTANTS = range(7, 11)
+
+
+def _generic_cases(seed0, count, nmax=24):
+    """Continuous data (no ties, blocks stable under tiny perturbations)."""
+    rng = np.random.default_rng(seed0)
+    for k in range(count):
+        n = int(rng.integers(1, nmax + 1))
+        y = rng.normal(0, 1, n) + (np.linspace(0, 2, n) if k % 2 else 0.0)
+        wk = k % 3
+        w = None if wk == 0 else (0.1 + rng.random(n) if wk == 1 else np.exp(4 * rng.random(n)))
+        g = rng.normal(0, 1, n)
+        yield y, w, g
+
+
+def _fd(fit, y, w, g, h):
+    """Central differences of L = g . fit(y, w) in every y_i and w_i."""
+    n = len(y)
+    dy = np.empty(n)
+    dw = None if w is None else np.empty(n)
+    for i in range(n):
+        e = np.zeros(n)
+        e[i] = h
+        dy[i] = (g @ fit(y + e, w) - g @ fit(y - e, w)) / (2 * h)
+        if w is not None:
+            dw[i] = (g @ fit(y, w + e) - g @ fit(y, w - e)) / (2 * h)
+    return dy, dw
+
+
+def pin_vjp_finite_differences(mutant=0, count=90):
+    fails = []
+    fit = lambda y, w: oracle.pava(y, w)[0]
+    for y, w, g in _generic_cases(71, count):
+        gy, gw = oracle.vjp(y, w, g, mutant=mutant)
+        dy, dw = _fd(fit, y, w, g, 1e-6)
+        tol = 1e-6 * (1.0 + np.abs(g).sum())
+        bad = np.abs(gy - dy).max() > tol or (w is not None and np.abs(gw - dw).max() > tol)
+        if bad:
+            fails.append(f"vjp finite differences n={len(y)} weighted={w is not None}")
+            if len(fails) > 3:
+                break
+    return fails
+
+
+def pin_vjp_brute_force_route(mutant=0, count=60):
+    """The same finite differences taken on the brute-force fit (n <= 10), so
+    the blocks the product averages over are pinned independently of PAVA."""
+    fails = []
+    fit = lambda y, w: oracle.brute_force(y, w)[0]
+    for y, w, g in _generic_cases(73, count, nmax=10):
+        gy, gw = oracle.vjp(y, w, g, mutant=mutant)
+        dy, dw = _fd(fit, y, w, g, 1e-6)
+        tol = 1e-6 * (1.0 + np.abs(g).sum())
+        if np.abs(gy - dy).max() > tol or (w is not None and np.abs(gw - dw).max() > tol):
+            fails.append(f"vjp brute-force route n={len(y)}")
+    return fails
+
+
+def pin_vjp_closed_forms(mutant=0):
+    fails = []
+    rng = np.random.default_rng(17)
+    n = 300
+    g = rng.normal(0, 1, n)
+    w = 0.2 + rng.random(n)
+    # strictly increasing: every element its own block, d/dy = g, d/dw = 0
+    y = np.sort(rng.random(n))
+    gy, gw = oracle.vjp(y, w, g, mutant=mutant)
+    if not (np.allclose(gy, g, rtol=1e-14, atol=1e-15) and np.allclose(gw, 0.0, atol=1e-15)):
+        fails.append("vjp increasing")
+    # strictly decreasing: one block; d/dy_i = w_i sum(g)/sum(w), d/dw_i = (y_i - mean) sum(g)/sum(w)
+    y = -np.sort(rng.random(n))
+    gy, gw = oracle.vjp(y, w, g, mutant=mutant)
+    r = g.sum() / w.sum()
+    m = (w * y).sum() / w.sum()
+    if not (np.allclose(gy, w * r, rtol=1e-12, atol=1e-14) and np.allclose(gw, (y - m) * r, rtol=1e-10, atol=1e-14)):
+        fails.append("vjp decreasing")
+    # unit weights, constant row: the mean of g everywhere
+    gy, gw = oracle.vjp(np.full(n, 0.5), None, g, mutant=mutant)
+    if not np.allclose(gy, g.mean(), rtol=1e-12, atol=1e-14) or gw is not None:
+        fails.append("vjp constant")
+    return fails
+
+
+def pin_vjp_block_sums(mutant=0):
+    """Over any given partition, d/dy summed over a block is G, and w-weighted
+    d/dw summed over a block is zero (z is the block's weighted mean)."""
+    fails = []
+    rng = np.random.default_rng(19)
+    for k in range(30):
+        n = int(rng.integers(2, 400))
+        y = rng.normal(0, 1, n)
+        w = 0.1 + rng.random(n)
+        g = rng.normal(0, 1, n)
+        starts = np.sort(rng.choice(np.arange(1, n), size=int(rng.integers(0, n // 3 + 1)), replace=False))
+        bid = np.zeros(n, np.int32)
+        bid[starts] = 1
+        bid = np.cumsum(bid).astype(np.int32)
+        gy, gw = oracle.vjp(y, w, g, block_id=bid, mutant=mutant)
+        for b in range(bid[-1] + 1):
+            idx = bid == b
+            if abs(gy[idx].sum() - g[idx].sum()) > 1e-12 * (1 + np.abs(g[idx]).sum()):
+                fails.append(f"vjp block sum d/dy block {b}")
+                break
+            if abs((w[idx] * gw[idx]).sum()) > 1e-12 * (1 + np.abs(w[idx] * gw[idx]).sum() + abs(g[idx].sum())):
+                fails.append(f"vjp block sum d/dw block {b}")
+                break
+    return fails
+
+
+VJP_PINS = (pin_vjp_finite_differences, pin_vjp_brute_force_route, pin_vjp_closed_forms,
+            pin_vjp_block_sums)
+
+
+@pytest.mark.parametrize("pin", VJP_PINS, ids=lambda p: p.__name__)
+def test_oracle_vjp_pin(pin):
+    fails = pin()
+    assert not fails, "\n".join(fails)
+
+
+def test_oracle_vjp_rows_match_single_rows():
+    y, w = inputs.calibration(3, 5000, 12)
+    g = np.random.default_rng(3).normal(0, 1, y.shape).astype(np.float32)
+    _, _, bid = oracle.fit_rows_f32(y, w)
+    gy, gw = oracle.vjp_rows_f32(y, w, g, bid)
+    for r in range(3):
+        a, b = oracle.vjp(y[r], w[r], g[r])
+        assert np.array_equal(gy[r], a) and np.array_equal(gw[r], b)
+    bid[1, :] = -1  # a non-finite row of the fit
+    gy, gw = oracle.vjp_rows_f32(y, w, g, bid)
+    assert np.all(np.isnan(gy[1])) and np.all(np.isnan(gw[1])) and not np.isnan(gy[[0, 2]]).any()
+
+
+@pytest.mark.parametrize("mutant", VJP_MUTANTS)
+def test_planted_vjp_mistakes_are_caught(mutant):
+    caught = [p.__name__ for p in (pin_vjp_closed_forms, pin_vjp_block_sums) if p(mutant=mutant)]
+    if not caught and pin_vjp_finite_differences(mutant=mutant, count=30):
+        caught.append("pin_vjp_finite_differences")
+    assert caught, f"mutant {mutant} passed every VJP pin"
