@@ -138,6 +138,51 @@ int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* o
 int iso_fit_noalloc(const float* y, const float* w, int64_t rows, int64_t n, float* out,
                     int32_t* block_id, void* stream, uint32_t flags);
 
+/*
+ * iso_vjp - the backward pass: the vector-Jacobian product of the fit (paper
+ * section 6, paragraph "Gradient"; validated as its appendix C describes).
+ * The fit is constant on its blocks, each block's value the weighted mean z of
+ * y over the block, so for an element i with G and W the sums of g and of w
+ * over its block:
+ *     grad_y[i] = w_i G / W ,        grad_w[i] = (y_i - z) G / W
+ * (wherever the blocks do not change; at a boundary between equal means the
+ * fit is not differentiable and the blocks of the forward call are used).
+ *   g         [rows*n] f32, device: the gradient with respect to the fit.
+ *   y         [rows*n] f32, device: the forward call's y; needed only for
+ *             grad_w (may be NULL when grad_w is NULL).
+ *   w         [rows*n] f32, device: the forward call's weights, or NULL for
+ *             unit weights.
+ *   block_id  [rows*n] int32, device: the block ids the forward call wrote
+ *             (iso_fit_ex or iso_fit_noalloc with a block_id buffer), for the
+ *             same y, w and flags.  A block starts at a row's first element
+ *             and wherever the id changes.  A row whose ids are negative (a
+ *             non-finite row of the forward call) gets NaN gradients.
+ *   grad_y    [rows*n] f32, device, written, or NULL.
+ *   grad_w    [rows*n] f32, device, written, or NULL (needs y and w).
+ *   workspace device buffer of iso_vjp_workspace_bytes(rows, n) bytes,
+ *             256-byte aligned, contents need no initialisation (NULL when
+ *             that size is 0: rows of at most 2048 elements).
+ *   stream    hipStream_t (NULL = the null stream).  The call only enqueues.
+ * A decreasing fit (ISO_F_DECREASING) has the same gradient formulas in y and
+ * w, so the same call serves it.  Sums are f64, without atomics (the result
+ * does not depend on scheduling); each output is rounded once to f32.
+ * Returns ISO_OK, ISO_ERR_ARG (NULL g or block_id, no output, grad_w without y
+ * or w, misaligned or overlapping buffers, bad sizes), ISO_ERR_WORKSPACE or
+ * ISO_ERR_HIP; nothing is launched on an error.
+ */
+int iso_vjp(const float* g, const float* y, const float* w, const int32_t* block_id, int64_t rows,
+            int64_t n, float* grad_y, float* grad_w, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* The same with f64 g, y, w and gradients (8-byte aligned). */
+int iso_vjp_f64(const double* g, const double* y, const double* w, const int32_t* block_id,
+                int64_t rows, int64_t n, double* grad_y, double* grad_w, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace iso_vjp and iso_vjp_f64 need for this shape (0 for
+ * rows of at most 2048 elements, or an empty or invalid shape). */
+size_t iso_vjp_workspace_bytes(int64_t rows, int64_t n);
+
 /* Bytes of device workspace iso_fit_ex needs for this shape and these flags
  * (weighted or not is part of the shape: pass ISO_F_WEIGHTED_HINT in flags
  * when w will be non-NULL).  Returns 0 for an empty or invalid shape. */

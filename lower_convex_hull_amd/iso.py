@@ -36,7 +36,7 @@ ISO_NOALLOC_BYTES = 64 << 20
 
 EXPORTS = ("iso_fit", "iso_fit_ex", "iso_fit_noalloc", "iso_workspace_bytes", "iso_status_str",
            "iso_release", "iso_chunk_size", "iso_short_row_max", "iso_timing_enable",
-           "iso_timing_read")
+           "iso_timing_read", "iso_vjp", "iso_vjp_f64", "iso_vjp_workspace_bytes")
 
 _lib = None
 
@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.iso_fit_ex.restype = ctypes.c_int
         L.iso_fit_noalloc.argtypes = [p, p, i64, i64, p, p, p, u32]
         L.iso_fit_noalloc.restype = ctypes.c_int
+        L.iso_vjp.argtypes = [p, p, p, p, i64, i64, p, p, p, sz, p]
+        L.iso_vjp.restype = ctypes.c_int
+        L.iso_vjp_f64.argtypes = [p, p, p, p, i64, i64, p, p, p, sz, p]
+        L.iso_vjp_f64.restype = ctypes.c_int
+        L.iso_vjp_workspace_bytes.argtypes = [i64, i64]
+        L.iso_vjp_workspace_bytes.restype = sz
         L.iso_workspace_bytes.argtypes = [i64, i64, u32]
         L.iso_workspace_bytes.restype = sz
         L.iso_status_str.argtypes = [ctypes.c_int]
@@ -89,6 +95,22 @@ def iso_fit_ex(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes, s
 
 def iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags) -> int:
     return lib().iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags)
+
+
+def iso_vjp(g_ptr, y_ptr, w_ptr, block_id_ptr, rows, n, grad_y_ptr, grad_w_ptr, ws_ptr, ws_bytes,
+            stream) -> int:
+    return lib().iso_vjp(g_ptr, y_ptr, w_ptr, block_id_ptr, rows, n, grad_y_ptr, grad_w_ptr, ws_ptr,
+                         ws_bytes, stream)
+
+
+def iso_vjp_f64(g_ptr, y_ptr, w_ptr, block_id_ptr, rows, n, grad_y_ptr, grad_w_ptr, ws_ptr,
+                ws_bytes, stream) -> int:
+    return lib().iso_vjp_f64(g_ptr, y_ptr, w_ptr, block_id_ptr, rows, n, grad_y_ptr, grad_w_ptr,
+                             ws_ptr, ws_bytes, stream)
+
+
+def iso_vjp_workspace_bytes(rows, n) -> int:
+    return lib().iso_vjp_workspace_bytes(rows, n)
 
 
 def iso_workspace_bytes(rows, n, flags=0) -> int:
@@ -171,3 +193,23 @@ def fit(y, w=None, *, block_ids: bool = False, flags: int = 0, out=None, ws=None
     if st < 0:
         raise IsoError(st)
     return (out, bid) if block_ids else out
+
+
+def vjp(g, y, w, block_id, *, grad_w: bool = False, stream=None):
+    """Backward pass over torch CUDA tensors (f32 or f64, like g): returns
+    grad_y, or (grad_y, grad_w) when grad_w.  block_id is the forward call's."""
+    import torch
+
+    g2 = g.reshape(1, -1) if g.dim() == 1 else g
+    rows, n = g2.shape
+    gy = torch.empty_like(g)
+    gw = torch.empty_like(g) if grad_w else None
+    nb = iso_vjp_workspace_bytes(rows, n)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=g.device)
+    fn = iso_vjp if g.dtype == torch.float32 else iso_vjp_f64
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = fn(g.data_ptr(), ptr(y), ptr(w), block_id.data_ptr(), rows, n, gy.data_ptr(), ptr(gw),
+            ws.data_ptr(), nb, _stream_handle(stream))
+    if st < 0:
+        raise IsoError(st)
+    return (gy, gw) if grad_w else gy

@@ -142,3 +142,45 @@ def block_ids_consistent(oracle_bid, gpu_bid, z64, y, delta_scale=1e-6) -> bool:
         if s not in oset and abs(z[s] - z[s - 1]) > delta:
             return False
     return True
+
+
+def _block_bounds(bid):
+    """Start of each block of one row (block ids: a start wherever the id changes)."""
+    bid = np.asarray(bid)
+    return np.concatenate([[0], np.flatnonzero(np.diff(bid) != 0) + 1])
+
+
+def vjp_tolerance(y, w, g, bid, out_eps=2.0 ** -24):
+    """Per-element bound on |GPU - oracle| for the vector-Jacobian product of one
+    row over the blocks bid: both sides form the block sums G = sum g,
+    W = sum w and S = sum w y in f64 in different orders, each off the exact sum
+    by at most m u sum|terms| (m terms, u = 2^-53), and round the result once to
+    the output type (out_eps: 2^-24 for f32, 2^-53 for f64).  Returns
+    (tol_gy, tol_gw); tol_gw is None for unit weights."""
+    u = 2.0 ** -53
+    y = np.asarray(y, np.float64)
+    g = np.asarray(g, np.float64)
+    wv = np.ones_like(y) if w is None else np.asarray(w, np.float64)
+    st = _block_bounds(bid)
+    m = np.diff(np.concatenate([st, [len(y)]])).astype(np.float64)
+    G = np.add.reduceat(g, st)
+    Ga = np.add.reduceat(np.abs(g), st)
+    W = np.add.reduceat(wv, st)
+    S = np.add.reduceat(wv * y, st)
+    Sa = np.add.reduceat(np.abs(wv * y), st)
+    eG = 2 * m * u * Ga  # sums on both sides
+    eW = 2 * m * u * W
+    eS = 2 * m * u * Sa
+    r = G / W
+    er = (eG + np.abs(r) * eW) / W * (1 + 1e-6)
+    z = S / W
+    ez = (eS + np.abs(z) * eW) / W * (1 + 1e-6)
+    rep = np.repeat(np.arange(len(st)), m.astype(np.int64))
+    gy = wv * r[rep]
+    tol_gy = 2 * out_eps * np.abs(gy) + wv * er[rep] + 1e-300
+    if w is None:
+        return tol_gy, None
+    d = y - z[rep]
+    gw = d * r[rep]
+    tol_gw = 2 * out_eps * np.abs(gw) + np.abs(d) * er[rep] + ez[rep] * (np.abs(r[rep]) + er[rep]) + 1e-300
+    return tol_gy, tol_gw

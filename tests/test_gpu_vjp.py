@@ -1,0 +1,239 @@
+"""GPU parity of the backward pass (iso_vjp, iso_vjp_f64) through the C ABI
+against the oracle's vector-Jacobian product (oracle_vjp: block averaging of the
+incoming gradient, paper section 6, "Gradient"), element by element.
+
+Following the paper's appendix C: the GPU gradient is compared with the
+oracle's over the GPU forward call's own blocks on every workload and family,
+and with the oracle's over its own blocks where the two partitions agree.  The
+tolerance is derived in tests/fitcheck.vjp_tolerance (f64 block sums in another
+order, one rounding to the output type)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lower_convex_hull_amd import inputs, iso
+from tests import fitcheck
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    iso.lib()
+    return t
+
+
+def forward_ids(torch, y, w, flags=0):
+    """Block ids of the GPU forward call (and its status)."""
+    yt = torch.from_numpy(np.ascontiguousarray(y, np.float32)).cuda()
+    wt = None if w is None else torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    rows, n = yt.shape
+    out = torch.empty_like(yt)
+    bid = torch.empty((rows, n), dtype=torch.int32, device="cuda")
+    ws = iso.workspace(rows, n, wt is not None, flags)
+    st = iso.iso_fit_ex(yt.data_ptr(), None if wt is None else wt.data_ptr(), rows, n, out.data_ptr(),
+                        bid.data_ptr(), ws.data_ptr(), ws.numel(), iso._stream_handle(None), flags)
+    torch.cuda.synchronize()
+    return st, bid.cpu().numpy()
+
+
+def gpu_vjp(torch, g, y, w, bid, grad_w, dtype=np.float32):
+    tt = torch.float32 if dtype == np.float32 else torch.float64
+    gt = torch.from_numpy(np.ascontiguousarray(g, dtype)).cuda()
+    yt = torch.from_numpy(np.ascontiguousarray(y, dtype)).cuda()
+    wt = None if w is None else torch.from_numpy(np.ascontiguousarray(w, dtype)).cuda()
+    bt = torch.from_numpy(np.ascontiguousarray(bid, np.int32)).cuda()
+    rows, n = gt.shape
+    gy = torch.full((rows, n), 12345.0, dtype=tt, device="cuda")  # every element must be written
+    gw = torch.full((rows, n), 12345.0, dtype=tt, device="cuda") if grad_w else None
+    nb = iso.iso_vjp_workspace_bytes(rows, n)
+    ws = torch.full((max(nb, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    fn = iso.iso_vjp if dtype == np.float32 else iso.iso_vjp_f64
+    st = fn(gt.data_ptr(), yt.data_ptr(), None if wt is None else wt.data_ptr(), bt.data_ptr(), rows, n,
+            gy.data_ptr(), None if gw is None else gw.data_ptr(), ws.data_ptr(), nb, iso._stream_handle(None))
+    torch.cuda.synchronize()
+    return st, gy.cpu().numpy(), (None if gw is None else gw.cpu().numpy())
+
+
+def check_vjp(torch, y, w, g, bid, name, dtype=np.float32):
+    """GPU VJP over blocks `bid` against the oracle over the same blocks."""
+    grad_w = w is not None
+    say(f"[vjp] {name} rows={y.shape[0]} n={y.shape[1]} weighted={grad_w} dtype={np.dtype(dtype).name}")
+    st, gy, gw = gpu_vjp(torch, g, y, w, bid, grad_w, dtype)
+    assert st == iso.ISO_OK, iso.iso_status_str(st)
+    eps = 2.0 ** -24 if dtype == np.float32 else 2.0 ** -53
+    for r in range(y.shape[0]):
+        wr = None if w is None else w[r]
+        if bid[r, 0] < 0:
+            assert np.all(np.isnan(gy[r])) and (gw is None or np.all(np.isnan(gw[r]))), (name, r)
+            continue
+        ry, rw = oracle.vjp(y[r].astype(np.float64), None if wr is None else wr.astype(np.float64),
+                            g[r].astype(np.float64), block_id=bid[r])
+        ty, tw = fitcheck.vjp_tolerance(y[r], wr, g[r], bid[r], out_eps=eps)
+        ey = np.abs(gy[r] - ry)
+        assert np.all(ey <= ty), f"{name} row {r}: d/dy error {ey.max():.3g} at {int(np.argmax(ey / ty))}"
+        if grad_w:
+            ew = np.abs(gw[r] - rw)
+            assert np.all(ew <= tw), f"{name} row {r}: d/dw error {ew.max():.3g} at {int(np.argmax(ew / tw))}"
+    return gy, gw
+
+
+def full(torch, y, w, name, seed, flags=0, own_blocks=False):
+    """Forward on the GPU, then the VJP over its blocks against the oracle."""
+    y = np.atleast_2d(np.asarray(y, np.float32))
+    if w is not None:
+        w = np.asarray(w, np.float32).reshape(y.shape)
+    st, bid = forward_ids(torch, y, w, flags)
+    assert st in (iso.ISO_OK, iso.ISO_WARN_NONFINITE)
+    g = np.random.default_rng(seed).standard_normal(y.shape).astype(np.float32)
+    gy, gw = check_vjp(torch, y, w, g, bid, name)
+    if own_blocks:
+        # data without near-ties: the GPU's blocks are the oracle's own, and the
+        # gradient matches the oracle's over its own blocks
+        ysign = -y if flags & iso.ISO_F_DECREASING else y
+        _, _, obid = oracle.fit_rows_f32(ysign, w)
+        for r in range(y.shape[0]):
+            assert np.array_equal(fitcheck._block_bounds(obid[r]), fitcheck._block_bounds(bid[r])), (name, r)
+    return gy, gw, bid
+
+
+# ------------------------------------------------------------------------------ workloads
+
+def test_vjp_c1_c2(torch):
+    full(torch, *inputs.config("c1_row4096_noisy"), "c1", 1, own_blocks=True)
+    full(torch, *inputs.config("c2_batch1024x1024_noisy"), "c2", 2, own_blocks=True)
+
+
+def test_vjp_c3_row1e7(torch):
+    y, w = inputs.config("c3_row1e7_noisy")
+    full(torch, y, w, "c3", 3, own_blocks=True)
+
+
+def test_vjp_c4_dense_is_identity(torch):
+    """Every element its own block: d/dy = g exactly (closed form)."""
+    y, w = inputs.config("c4_row1e7_dense")
+    st, bid = forward_ids(torch, y, w)
+    g = np.random.default_rng(4).standard_normal(y.shape).astype(np.float32)
+    st, gy, _ = gpu_vjp(torch, g, y, None, bid, False)
+    assert st == 0 and np.array_equal(gy, g)
+
+
+def test_vjp_c5_full_batch(torch):
+    """The 256 x 2^20 calibration batch, weighted: d/dy and d/dw of every row."""
+    y, w = inputs.config("c5_calib256x2p20")
+    st, bid = forward_ids(torch, y, w)
+    assert st == 0
+    g = np.random.default_rng(5).standard_normal(y.shape).astype(np.float32)
+    say("[vjp] c5 256 x 2^20 weighted")
+    st, gy, gw = gpu_vjp(torch, g, y, w, bid, True)
+    assert st == 0
+    for r0 in range(0, y.shape[0], 32):
+        sl = slice(r0, r0 + 32)
+        ry, rw = oracle.vjp_rows_f32(y[sl], w[sl], g[sl], bid[sl])
+        for k in range(ry.shape[0]):
+            r = r0 + k
+            ty, tw = fitcheck.vjp_tolerance(y[r], w[r], g[r], bid[r])
+            assert np.all(np.abs(gy[r] - ry[k]) <= ty), f"c5 row {r} d/dy"
+            assert np.all(np.abs(gw[r] - rw[k]) <= tw), f"c5 row {r} d/dw"
+
+
+# ------------------------------------------------------------------------------ families and edges
+
+@pytest.mark.parametrize("n", [1, 2, 7, 2047, 2048, 2049, 4096, 6145, 100_003])
+@pytest.mark.parametrize("fam", ["gaussian", "sawtooth", "constant", "decreasing", "increasing",
+                                 "random_walk", "cliff", "piecewise"])
+def test_vjp_families(torch, fam, n):
+    for k, wk in enumerate(inputs.WEIGHTINGS):
+        rows = 3
+        y = np.stack([inputs.family(fam, n, 500 + 10 * k + r) for r in range(rows)])
+        w = None if wk == "none" else np.stack([inputs.weights(wk, n, 600 + 10 * k + r) for r in range(rows)])
+        full(torch, y, w, f"{fam}/{wk}/{n}", 700 + k)
+
+
+@pytest.mark.parametrize("shape", [(5000, 1), (3000, 16), (777, 37), (64, 1000), (9, 2048)])
+def test_vjp_batches_of_short_rows(torch, shape):
+    rows, n = shape
+    y, _ = inputs.noisy(rows, n, 70 + n)
+    w = inputs.weights("exp", rows * n, 71 + n).reshape(rows, n)
+    full(torch, y, None, f"short {rows}x{n}", 72 + n)
+    full(torch, y, w, f"short-w {rows}x{n}", 73 + n)
+
+
+def test_vjp_given_partitions_across_tiles(torch):
+    """Partitions chosen directly (the product is defined for any partition):
+    blocks that start exactly at tile edges, span many tiles, or are single
+    elements next to tile edges."""
+    rng = np.random.default_rng(8)
+    T = 2048
+    n = 9 * T + 5
+    rows = 6
+    y = rng.normal(0, 1, (rows, n)).astype(np.float32)
+    w = (0.1 + rng.random((rows, n))).astype(np.float32)
+    g = rng.standard_normal((rows, n)).astype(np.float32)
+    starts = [
+        [0],                                             # one block over the row
+        [0] + [k * T for k in range(1, 10)],             # a block per tile, on the edges
+        [0, T - 1, T, T + 1, 3 * T - 1, 3 * T, 8 * T + 4],  # single elements at edges
+        [0] + list(range(1, n)),                         # every element a block
+        sorted(set([0] + rng.choice(np.arange(1, n), 40, replace=False).tolist())),
+        [0, 5 * T + 17],                                 # two blocks, one spanning five tiles
+    ]
+    bid = np.zeros((rows, n), np.int32)
+    for r, s in enumerate(starts):
+        f = np.zeros(n, np.int32)
+        f[s] = 1
+        bid[r] = np.cumsum(f) - 1
+    check_vjp(torch, y, w, g, bid, "given partitions")
+    check_vjp(torch, y, None, g, bid, "given partitions, unit weights")
+    check_vjp(torch, y.astype(np.float64), w.astype(np.float64), g.astype(np.float64), bid,
+              "given partitions f64", dtype=np.float64)
+
+
+def test_vjp_f64_against_oracle_blocks(torch):
+    """iso_vjp_f64 over the oracle's own f64 blocks, accuracy of f64 sums."""
+    rng = np.random.default_rng(9)
+    for n in (300, 2048, 50_000):
+        rows = 4
+        y = np.cumsum(rng.normal(0, 1, (rows, n)), axis=1) * 0.1 + np.linspace(0, 3, n)
+        w = np.exp(4 * rng.random((rows, n)))
+        g = rng.standard_normal((rows, n))
+        bid = np.stack([oracle.pava(y[r], w[r])[1] for r in range(rows)])
+        check_vjp(torch, y, w, g, bid, f"f64 n={n}", dtype=np.float64)
+
+
+def test_vjp_nonfinite_rows_and_decreasing(torch):
+    y, _ = inputs.noisy(4, 7000, 12)
+    y[2, 100] = np.nan
+    full(torch, y, None, "nan row", 13)
+    yd = y[:, ::-1].copy()
+    yd[2, :] = 0.5
+    full(torch, yd, None, "decreasing", 14, flags=iso.ISO_F_DECREASING, own_blocks=True)
+
+
+def test_vjp_argument_errors(torch):
+    g = torch.zeros((2, 5000), dtype=torch.float32, device="cuda")
+    b = torch.zeros((2, 5000), dtype=torch.int32, device="cuda")
+    out = torch.zeros_like(g)
+    nb = iso.iso_vjp_workspace_bytes(2, 5000)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sh = iso._stream_handle(None)
+    assert iso.iso_vjp(None, None, None, b.data_ptr(), 2, 5000, out.data_ptr(), None, ws.data_ptr(), nb, sh) == iso.ISO_ERR_ARG
+    assert iso.iso_vjp(g.data_ptr(), None, None, b.data_ptr(), 2, 5000, None, None, ws.data_ptr(), nb, sh) == iso.ISO_ERR_ARG
+    assert iso.iso_vjp(g.data_ptr(), None, None, b.data_ptr(), 2, 5000, None, out.data_ptr(), ws.data_ptr(), nb, sh) == iso.ISO_ERR_ARG
+    assert iso.iso_vjp(g.data_ptr(), None, None, b.data_ptr(), 2, 5000, g.data_ptr(), None, ws.data_ptr(), nb, sh) == iso.ISO_ERR_ARG
+    assert iso.iso_vjp(g.data_ptr(), None, None, b.data_ptr(), 2, 5000, out.data_ptr(), None, ws.data_ptr(), nb - 1, sh) == iso.ISO_ERR_WORKSPACE
+    assert iso.iso_vjp(g.data_ptr(), None, None, b.data_ptr(), 0, 5000, out.data_ptr(), None, None, 0, sh) == iso.ISO_OK
+    torch.cuda.synchronize()
+    assert float(out.abs().sum()) == 0.0
