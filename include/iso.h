@@ -18,11 +18,13 @@
  *   - y, w, out, block_id are DEVICE pointers (hipMalloc'd or torch CUDA
  *     tensors), row-major and contiguous: element (r, i) is at r*n + i.  They
  *     are caller-owned; the library never frees or retains them.
- *   - y, w, out are float32 and must be 4-byte aligned; block_id is int32.
+ *   - y, w, out are float32 and must be 4-byte aligned (the _f64 entry points:
+ *     float64, 8-byte aligned); block_id is int32.
  *   - w == NULL means unit weights.
  *   - The fit is accumulated in f64 and each output value is rounded once to
- *     float32 (round to nearest even), as the paper's section 6 ("Output")
- *     asks.  The output is not forced to be monotone (same section).
+ *     the output type (round to nearest even), as the paper's section 6
+ *     ("Output") asks.  The output is not forced to be monotone (same
+ *     section).
  *   - block_id (optional, NULL = not written): for each element, the 0-based
  *     index of its block (hull edge) within its row; non-decreasing along the
  *     row, +1 at every block start.  The paper's one-byte block-start flag
@@ -117,6 +119,19 @@ int iso_fit(const float* y, const float* w, int64_t rows, int64_t n, float* out)
 int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* out,
                int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
                uint32_t flags);
+
+/*
+ * iso_fit_ex_f64, iso_fit_f64 - the same fits with f64 y, w and out (8-byte
+ * aligned), through the same kernels (the paper's operator takes f32 and f64
+ * in one code path, section 6).  Every sum and predicate is f64 either way;
+ * with f64 input the products w_i y_i are rounded in f64, and each output is
+ * the f64 slope itself.  The workspace is the same as for f32
+ * (iso_workspace_bytes).  Statuses and flags as for iso_fit_ex / iso_fit.
+ */
+int iso_fit_ex_f64(const double* y, const double* w, int64_t rows, int64_t n, double* out,
+                   int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
+                   uint32_t flags);
+int iso_fit_f64(const double* y, const double* w, int64_t rows, int64_t n, double* out);
 
 /*
  * iso_fit_noalloc - iso_fit_ex without a caller workspace and without any

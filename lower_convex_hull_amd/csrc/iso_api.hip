@@ -182,20 +182,23 @@ Cache& cache() {
 
 // The fit on `stream` with `workspace`: argument checks, launches, and (without
 // ISO_F_NOCHECK) the data check.  Allocates nothing, on the device or the host.
-int fit_body(const float* y, const float* w, int64_t rows, int64_t n, float* out,
-             int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
-             uint32_t flags) {
+// T is the element type of y, w and out (float or double).
+template <typename T>
+int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* block_id,
+             void* workspace, size_t workspace_bytes, void* stream, uint32_t flags) {
     if (!y || !out || rows < 0 || n < 0 || (flags & ~kKnownFlags)) return ISO_ERR_ARG;
     if (rows == 0 || n == 0) return ISO_OK;
     const bool weighted = w != nullptr;
     const bool copy_control = (flags & ISO_F_COPY_CONTROL) != 0;
     Plan p;
     if (!plan(rows, n, weighted, copy_control, &p)) return ISO_ERR_ARG;
-    const size_t nb = (size_t)rows * (size_t)n * sizeof(float);
-    if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, nb, y, nb) ||
-        overlaps(block_id, nb, w, nb) || overlaps(block_id, nb, out, nb))
+    const size_t nb = (size_t)rows * (size_t)n * sizeof(T);
+    const size_t ib = (size_t)rows * (size_t)n * sizeof(int32_t);
+    if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, ib, y, nb) ||
+        overlaps(block_id, ib, w, nb) || overlaps(block_id, ib, out, nb))
         return ISO_ERR_ARG;
-    if (((uintptr_t)y | (uintptr_t)out | (uintptr_t)w | (uintptr_t)block_id) & 3u) return ISO_ERR_ARG;
+    if (((uintptr_t)y | (uintptr_t)out | (uintptr_t)w) & (sizeof(T) - 1)) return ISO_ERR_ARG;
+    if ((uintptr_t)block_id & 3u) return ISO_ERR_ARG;
     if (!workspace || workspace_bytes < p.bytes) return ISO_ERR_WORKSPACE;
     if ((uintptr_t)workspace % kAlign) return ISO_ERR_ARG;
 
@@ -204,11 +207,11 @@ int fit_body(const float* y, const float* w, int64_t rows, int64_t n, float* out
     int32_t* row_flag = at<int32_t>(workspace, p.off_row_flag);
     hipError_t e;
     if (!p.long_rows) {
-        e = iso::launch_short(y, w, rows, n, sign, out, block_id, row_flag, st);
+        e = iso::launch_short<T>(y, w, rows, n, sign, out, block_id, row_flag, st);
     } else {
         iso::LongShape sh{rows, n, p.m, weighted, sign};
         iso::LongWs ws = long_ws(workspace, p, weighted, copy_control);
-        e = iso::launch_long(y, w, sh, ws, out, block_id, copy_control, st);
+        e = iso::launch_long<T>(y, w, sh, ws, out, block_id, copy_control, st);
     }
     if (e != hipSuccess) return ISO_ERR_HIP;
     if (flags & ISO_F_NOCHECK) return ISO_OK;
@@ -256,6 +259,33 @@ void* scratch_ptr() {
         t.ptr[dev] = q;
     }
     return t.ptr[dev];
+}
+
+// The blocking fit with the per-device cached workspace (iso_fit, iso_fit_f64).
+template <typename T>
+int cached_fit(const T* y, const T* w, int64_t rows, int64_t n, T* out) {
+    if (!y || !out || rows < 0 || n < 0) return ISO_ERR_ARG;
+    if (rows == 0 || n == 0) return ISO_OK;
+    Plan p;
+    if (!plan(rows, n, w != nullptr, false, &p)) return ISO_ERR_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ISO_ERR_HIP;
+    Cache& c = cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    if ((size_t)dev >= c.ptr.size()) {
+        c.ptr.resize(dev + 1, nullptr);
+        c.bytes.resize(dev + 1, 0);
+    }
+    if (c.bytes[dev] < p.bytes) {
+        if (c.ptr[dev]) (void)hipFree(c.ptr[dev]);
+        c.ptr[dev] = nullptr;
+        c.bytes[dev] = 0;
+        void* q = nullptr;
+        if (hipMalloc(&q, p.bytes) != hipSuccess) return ISO_ERR_NOMEM;
+        c.ptr[dev] = q;
+        c.bytes[dev] = p.bytes;
+    }
+    return fit_body<T>(y, w, rows, n, out, nullptr, c.ptr[dev], c.bytes[dev], nullptr, 0u);
 }
 
 }  // namespace
@@ -348,7 +378,13 @@ size_t iso_workspace_bytes(int64_t rows, int64_t n, uint32_t flags) {
 int iso_fit_ex(const float* y, const float* w, int64_t rows, int64_t n, float* out,
                int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
                uint32_t flags) {
-    return fit_body(y, w, rows, n, out, block_id, workspace, workspace_bytes, stream, flags);
+    return fit_body<float>(y, w, rows, n, out, block_id, workspace, workspace_bytes, stream, flags);
+}
+
+int iso_fit_ex_f64(const double* y, const double* w, int64_t rows, int64_t n, double* out,
+                   int32_t* block_id, void* workspace, size_t workspace_bytes, void* stream,
+                   uint32_t flags) {
+    return fit_body<double>(y, w, rows, n, out, block_id, workspace, workspace_bytes, stream, flags);
 }
 
 int iso_fit_noalloc(const float* y, const float* w, int64_t rows, int64_t n, float* out,
@@ -360,32 +396,15 @@ int iso_fit_noalloc(const float* y, const float* w, int64_t rows, int64_t n, flo
     if (p.bytes > (size_t)ISO_NOALLOC_BYTES) return ISO_ERR_WORKSPACE;
     void* ws = scratch_ptr();
     if (!ws) return ISO_ERR_HIP;
-    return fit_body(y, w, rows, n, out, block_id, ws, (size_t)ISO_NOALLOC_BYTES, stream, flags);
+    return fit_body<float>(y, w, rows, n, out, block_id, ws, (size_t)ISO_NOALLOC_BYTES, stream, flags);
 }
 
 int iso_fit(const float* y, const float* w, int64_t rows, int64_t n, float* out) {
-    if (!y || !out || rows < 0 || n < 0) return ISO_ERR_ARG;
-    if (rows == 0 || n == 0) return ISO_OK;
-    Plan p;
-    if (!plan(rows, n, w != nullptr, false, &p)) return ISO_ERR_ARG;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ISO_ERR_HIP;
-    Cache& c = cache();
-    std::lock_guard<std::mutex> lock(c.mu);
-    if ((size_t)dev >= c.ptr.size()) {
-        c.ptr.resize(dev + 1, nullptr);
-        c.bytes.resize(dev + 1, 0);
-    }
-    if (c.bytes[dev] < p.bytes) {
-        if (c.ptr[dev]) (void)hipFree(c.ptr[dev]);
-        c.ptr[dev] = nullptr;
-        c.bytes[dev] = 0;
-        void* q = nullptr;
-        if (hipMalloc(&q, p.bytes) != hipSuccess) return ISO_ERR_NOMEM;
-        c.ptr[dev] = q;
-        c.bytes[dev] = p.bytes;
-    }
-    return iso_fit_ex(y, w, rows, n, out, nullptr, c.ptr[dev], c.bytes[dev], nullptr, 0u);
+    return cached_fit<float>(y, w, rows, n, out);
+}
+
+int iso_fit_f64(const double* y, const double* w, int64_t rows, int64_t n, double* out) {
+    return cached_fit<double>(y, w, rows, n, out);
 }
 
 void iso_release(void) {

@@ -122,18 +122,21 @@ struct IncSrc {
     const int32_t* cflag;  // chunk flags of the row (null: every chunk has a slot)
     const double* ckS;     // checkpoints of the row's chunks, kLongNT + 1 each
     const double* ckW;
-    const float* y;        // the row's elements
-    const float* w;
+    const void* y;         // the row's elements (f32, or f64 when f64)
+    const void* w;
     float sign;
+    int f64;
 };
 
 // ... for the chunks j0, j0+1, ... of a row (chunk j0 is chunk 0 of the view)
 __device__ __forceinline__ IncSrc inc_src(const LongWs& ws, int64_t row, int m, int j0) {
     const int64_t cb = row * m + j0;
     const int64_t eb = row * ws.n + (int64_t)j0 * kChunk;
+    const size_t es = ws.f64 ? 8 : 4;
     return IncSrc{ws.chunk_flag + cb, ws.ck_S + cb * (kLongNT + 1),
-                  ws.ck_W ? ws.ck_W + cb * (kLongNT + 1) : nullptr, ws.y + eb,
-                  ws.w ? ws.w + eb : nullptr, ws.sign};
+                  ws.ck_W ? ws.ck_W + cb * (kLongNT + 1) : nullptr,
+                  static_cast<const char*>(ws.y) + eb * es,
+                  ws.w ? static_cast<const char*>(ws.w) + eb * es : nullptr, ws.sign, ws.f64};
 }
 
 struct RowView {
@@ -146,6 +149,29 @@ struct RowView {
     const double* stW;
     bool weighted;
     IncSrc inc;
+
+    // The sums of elements 0..b of a thread's run, in the chunk kernel's order
+    // and arithmetic (lw: the weights' sum when weighted).
+    template <typename T>
+    __device__ __forceinline__ double inc_sum(const T* gy, const T* gw, int b, double& lw) const {
+        double ls = 0.0;
+        lw = 0.0;
+        const T sg = (T)inc.sign;
+        for (int t = 0; t <= b; ++t) {
+            T yy = gy[t];
+            if (!isfinite(yy)) yy = T(0);
+            const T yv = sg * yy;
+            if (weighted) {
+                T ww = gw[t];
+                if (!(ww > T(0) && isfinite(ww))) ww = T(1);
+                ls += (double)ww * (double)yv;
+                lw += (double)ww;
+            } else {
+                ls += (double)yv;
+            }
+        }
+        return ls;
+    }
 
     // Point k of strictly increasing chunk j (chunk-relative), summed exactly
     // as the chunk kernel summed it: its thread's checkpoint plus that
@@ -161,21 +187,14 @@ struct RowView {
             p.w = weighted ? inc.ckW[c + 1] : (double)k;
             return p;
         }
-        const float* gy = inc.y + (int64_t)j * kChunk + L * P;
-        const float* gw = weighted ? inc.w + (int64_t)j * kChunk + L * P : nullptr;
+        const int64_t e0 = (int64_t)j * kChunk + L * P;
         double ls = 0.0, lw = 0.0;
-        for (int t = 0; t <= b; ++t) {
-            float yy = gy[t];
-            if (!isfinite(yy)) yy = 0.0f;
-            const float yv = inc.sign * yy;
-            if (weighted) {
-                float ww = gw[t];
-                if (!(ww > 0.0f && isfinite(ww))) ww = 1.0f;
-                ls += (double)ww * (double)yv;
-                lw += (double)ww;
-            } else {
-                ls += (double)yv;
-            }
+        if (inc.f64) {
+            ls = inc_sum<double>(static_cast<const double*>(inc.y) + e0,
+                                 weighted ? static_cast<const double*>(inc.w) + e0 : nullptr, b, lw);
+        } else {
+            ls = inc_sum<float>(static_cast<const float*>(inc.y) + e0,
+                                weighted ? static_cast<const float*>(inc.w) + e0 : nullptr, b, lw);
         }
         p.s = inc.ckS[c] + ls;
         p.w = weighted ? inc.ckW[c] + lw : (double)k;

@@ -109,57 +109,68 @@ struct HullOut {
     bool fail;
 };
 
-// Loads the block's elements, forms the block-relative cumulative sums, and
-// builds the block's lower hull.  Returns this thread's element values (sign
-// applied, sanitised) in yv and its points' S (and W) in ps/pw: ps[b] is point
-// base+b+1.
-template <int NT, int P, bool WT, int MODE>
-__device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, const float* __restrict__ gy,
-                              const float* __restrict__ gw, int len, float sign, float (&yv)[P],
+// Loads the block's elements (T = float or double), forms the block-relative
+// cumulative sums, and builds the block's lower hull.  Returns this thread's
+// element values (sign applied, sanitised) in yv and its points' S (and W) in
+// ps/pw: ps[b] is point base+b+1.
+template <typename T, int P>
+__device__ __forceinline__ void load_elems(const T* __restrict__ p, T (&v)[P]) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int q = 0; q < P / 4; ++q) {
+            const float4 t = reinterpret_cast<const float4*>(p)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < P / 2; ++q) {
+            const double2 t = reinterpret_cast<const double2*>(p)[q];
+            v[2 * q] = t.x; v[2 * q + 1] = t.y;
+        }
+    }
+}
+
+template <int NT, int P, bool WT, int MODE, typename T>
+__device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, const T* __restrict__ gy,
+                              const T* __restrict__ gw, int len, float sign, T (&yv)[P],
                               double (&ps)[P], double (&pw)[P], double& s0, double& w0) {
     constexpr int RS = P + 1;
     const int L = threadIdx.x;
     const int base = L * P;
-    float wv[P];
+    const T sg = (T)sign;
+    T wv[P];
     int bad = 0;
     if (threadIdx.x == 0) sm.flag = 0;
     // a full block (no padding) takes loops without per-element range tests
     const bool full = len == NT * P;
 
     // ---- load (each thread its P consecutive elements) and check the data
-    float yr[P], wr[P];
+    T yr[P], wr[P];
     const bool whole = base + P <= len;
     if (P % 4 == 0 && whole && ((((uintptr_t)(gy + base)) | (WT ? (uintptr_t)(gw + base) : 0)) & 15u) == 0) {
-#pragma unroll
-        for (int q = 0; q < P / 4; ++q) {
-            float4 v = reinterpret_cast<const float4*>(gy + base)[q];
-            yr[4 * q] = v.x; yr[4 * q + 1] = v.y; yr[4 * q + 2] = v.z; yr[4 * q + 3] = v.w;
-            if (WT) {
-                float4 u = reinterpret_cast<const float4*>(gw + base)[q];
-                wr[4 * q] = u.x; wr[4 * q + 1] = u.y; wr[4 * q + 2] = u.z; wr[4 * q + 3] = u.w;
-            }
-        }
+        load_elems<T, P>(gy + base, yr);
+        if (WT) load_elems<T, P>(gw + base, wr);
     } else {
 #pragma unroll
         for (int b = 0; b < P; ++b) {
             int e = base + b;
-            yr[b] = e < len ? gy[e] : 0.0f;
-            if (WT) wr[b] = e < len ? gw[e] : 0.0f;
+            yr[b] = e < len ? gy[e] : T(0);
+            if (WT) wr[b] = e < len ? gw[e] : T(0);
         }
     }
     // the element before this thread's first (for the increasing test)
-    float yp = (L > 0 && base <= len) ? gy[base - 1] : 0.0f;
-    if (!isfinite(yp)) yp = 0.0f;
-    yp *= sign;
+    T yp = (L > 0 && base <= len) ? gy[base - 1] : T(0);
+    if (!isfinite(yp)) yp = T(0);
+    yp *= sg;
     if (full) {
 #pragma unroll
         for (int b = 0; b < P; ++b) {
-            float yy = yr[b];
-            float ww = 1.0f;
+            T yy = yr[b];
+            T ww = T(1);
             if (WT) ww = wr[b];
-            if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
-            if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
-            yv[b] = sign * yy;
+            if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = T(0); }
+            if (WT && !(ww > T(0) && isfinite(ww))) { bad |= kFlagWeight; ww = T(1); }
+            yv[b] = sg * yy;
             wv[b] = ww;
         }
     } else {
@@ -167,16 +178,16 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
         for (int b = 0; b < P; ++b) {
             int e = base + b;
             bool in = e < len;
-            float yy = yr[b];
-            float ww = 1.0f;
+            T yy = yr[b];
+            T ww = T(1);
             if (WT) ww = wr[b];
             if (in) {
-                if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = 0.0f; }
-                if (WT && !(ww > 0.0f && isfinite(ww))) { bad |= kFlagWeight; ww = 1.0f; }
+                if (!isfinite(yy)) { bad |= kFlagNonfinite; yy = T(0); }
+                if (WT && !(ww > T(0) && isfinite(ww))) { bad |= kFlagWeight; ww = T(1); }
             } else {
-                ww = 0.0f;
+                ww = T(0);
             }
-            yv[b] = sign * yy;
+            yv[b] = sg * yy;
             wv[b] = ww;
         }
     }
@@ -186,7 +197,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
 #pragma unroll
     for (int b = 0; b < P; ++b) {
         if (WT) {
-            ls += (double)wv[b] * (double)yv[b];  // exact product of two f32
+            ls += (double)wv[b] * (double)yv[b];  // exact for f32 inputs (24 + 24 bits)
             lw += (double)wv[b];
             pw[b] = lw;
         } else {
@@ -500,7 +511,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     // from registers, a pop reloads the entry under the new top
     const int r0 = L * RS;
     {
-        Pt T{w0, s0}, U{0.0, 0.0};
+        Pt Top{w0, s0}, U{0.0, 0.0};  // the stack's top and the entry under it
         sm.S[r0] = s0;
         if (WT) sm.W[r0] = w0;
         sm.idx[r0] = (uint16_t)base;
@@ -509,17 +520,17 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
         for (int b = 1; b <= P; ++b) {
             if (!((cand >> b) & 1u)) continue;
             const Pt Cp{WT ? pw[b - 1] : (double)min(base + b, len), ps[b - 1]};
-            while (dep >= 2 && cross3(U, T, Cp) <= 0.0) {
+            while (dep >= 2 && cross3(U, Top, Cp) <= 0.0) {
                 --dep;
-                T = U;
+                Top = U;
                 if (dep >= 2) U = ent(r0 + dep - 2);
             }
             sm.S[r0 + dep] = Cp.s;
             if (WT) sm.W[r0 + dep] = Cp.w;
             sm.idx[r0 + dep] = (uint16_t)(base + b);
             ++dep;
-            U = T;
-            T = Cp;
+            U = Top;
+            Top = Cp;
         }
         sm.cnt[L] = dep;
     }
@@ -640,11 +651,11 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
 // LDS and few registers, so that many workgroups share a CU; a chunk it gives
 // up on gets the chunk flag kChunkRedo and a window header of h = 0, and is
 // rebuilt with chains and merges (MODE kHullChains) by the first merge stage
-// (NT = 1024, P = 4) or by the fallback kernel.  Every chunk's flag and window
+// (NT = 1024, P = 4; f32 input) or by the fallback kernel.  Every chunk's flag and window
 // header are written in every call, so the rebuild depends on no earlier call.
 // ----------------------------------------------------------------------------
-template <int NT, int P, int MODE, bool WT>
-__device__ __forceinline__ void chunk_hull(const float* __restrict__ y, const float* __restrict__ w,
+template <int NT, int P, int MODE, bool WT, typename T>
+__device__ __forceinline__ void chunk_hull(const T* __restrict__ y, const T* __restrict__ w,
                                            int64_t n, int m, float sign, const LongWs& ws,
                                            int full_slots, HullSmem<NT, P, WT, MODE>& sm,
                                            int64_t gid /* row * m + chunk */) {
@@ -654,9 +665,9 @@ __device__ __forceinline__ void chunk_hull(const float* __restrict__ y, const fl
     const int j = (int)(gid - row * m);
     const int64_t off = row * n + (int64_t)j * C;
     const int len = (int)min((int64_t)C, n - (int64_t)j * C);
-    float yv[P];
+    T yv[P];
     double ps[P], pw[P], s0, w0;
-    const HullOut ho = block_hull<NT, P, WT, MODE>(sm, y + off, WT ? w + off : nullptr, len, sign, yv,
+    const HullOut ho = block_hull<NT, P, WT, MODE, T>(sm, y + off, WT ? w + off : nullptr, len, sign, yv,
                                                    ps, pw, s0, w0);
     const int L = threadIdx.x;
     const int base = L * P;

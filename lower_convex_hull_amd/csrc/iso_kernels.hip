@@ -36,32 +36,33 @@ namespace {
 // ----------------------------------------------------------------------------
 // Short rows: the whole row in one workgroup, fit written directly.
 // ----------------------------------------------------------------------------
-template <int NT, int P, bool WT>
-__global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
-                                                   const float* __restrict__ w, int64_t n,
-                                                   float sign, float* __restrict__ out,
+template <int NT, int P, bool WT, typename T>
+__global__ __launch_bounds__(NT) void k_short_rows(const T* __restrict__ y,
+                                                   const T* __restrict__ w, int64_t n,
+                                                   float sign, T* __restrict__ out,
                                                    int32_t* __restrict__ block_id,
                                                    int32_t* __restrict__ row_flag) {
     __shared__ HullSmem<NT, P, WT, kHullBoth> sm;
     const int64_t row = blockIdx.x;
-    const float* gy = y + row * n;
-    const float* gw = WT ? w + row * n : nullptr;
+    const T* gy = y + row * n;
+    const T* gw = WT ? w + row * n : nullptr;
     const int len = (int)n;
-    float yv[P];
+    const T sg = (T)sign;
+    T yv[P];
     double ps[P], pw[P], s0, w0;
-    const HullOut ho = block_hull<NT, P, WT, kHullBoth>(sm, gy, gw, len, sign, yv, ps, pw, s0, w0);
+    const HullOut ho = block_hull<NT, P, WT, kHullBoth, T>(sm, gy, gw, len, sign, yv, ps, pw, s0, w0);
 
     const int L = threadIdx.x;
     const int base = L * P;
     const int flag = sm.flag;
     if (L == 0) row_flag[row] = flag;
-    float* go = out + row * n;
+    T* go = out + row * n;
     int32_t* gb = block_id ? block_id + row * n : nullptr;
     if (flag & kFlagNonfinite) {
         for (int b = 0; b < P; ++b) {
             int e = base + b;
             if (e < len) {
-                go[e] = __builtin_nanf("");
+                go[e] = (T)__builtin_nan("");
                 if (gb) gb[e] = -1;
             }
         }
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
         for (int b = 0; b < P; ++b) {
             const int e = base + b;
             if (e < len) {
-                go[e] = sign * yv[b];
+                go[e] = sg * yv[b];
                 if (gb) gb[e] = e;
             }
         }
@@ -89,50 +90,50 @@ __global__ __launch_bounds__(NT) void k_short_rows(const float* __restrict__ y,
     }
     int q = lo - 1;
     int qs = -1;
-    float slope = 0.0f;
+    T slope = T(0);
 #pragma unroll
     for (int b = 0; b < P; ++b) {
         const int e = base + b;
         if (e >= len) break;
         while ((int)sm.idx[q + 1] <= e) ++q;  // vertex q <= e < vertex q+1
         const int ka = sm.idx[q], kb = sm.idx[q + 1];
-        float val;
+        T val;
         if (ka == e && kb == e + 1) {
             val = yv[b];  // both ends are vertices: the edge is the element itself
         } else {
             if (qs != q) {
                 const double dw = WT ? sm.W[q + 1] - sm.W[q] : (double)(min(kb, len) - ka);
-                slope = (float)((sm.S[q + 1] - sm.S[q]) / dw);
+                slope = (T)((sm.S[q + 1] - sm.S[q]) / dw);
                 qs = q;
             }
             val = slope;
         }
-        go[e] = sign * val;
+        go[e] = sg * val;
         if (gb) gb[e] = q;
     }
 }
 
 
-template <bool WT>
-__global__ __launch_bounds__(kLongNT, WT ? 2 : 4) void k_chunk_hulls(const float* __restrict__ y,
-                                                         const float* __restrict__ w, int64_t n,
-                                                         int m, float sign, LongWs ws, int full_slots) {
+template <bool WT, typename T>
+__global__ __launch_bounds__(kLongNT, WT || sizeof(T) == 8 ? 2 : 4) void k_chunk_hulls(
+    const T* __restrict__ y, const T* __restrict__ w, int64_t n, int m, float sign, LongWs ws,
+    int full_slots) {
     __shared__ HullSmem<kLongNT, kLongP, WT, kHullQuick> sm;
-    chunk_hull<kLongNT, kLongP, kHullQuick, WT>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x);
+    chunk_hull<kLongNT, kLongP, kHullQuick, WT, T>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x);
 }
 
 // The fallback for rows the first merge stage does not take (rows beyond the
 // two-stage merge, and the vertex-copying control): a fixed grid walks the
 // chunks and rebuilds the ones the chunk kernel marked in this call.
-template <bool WT>
-__global__ __launch_bounds__(kLongNT) void k_chunk_redo(const float* __restrict__ y,
-                                                        const float* __restrict__ w, int64_t n,
+template <bool WT, typename T>
+__global__ __launch_bounds__(kLongNT) void k_chunk_redo(const T* __restrict__ y,
+                                                        const T* __restrict__ w, int64_t n,
                                                         int m, float sign, LongWs ws, int full_slots,
                                                         int64_t nchunks) {
     __shared__ HullSmem<kLongNT, kLongP, WT, kHullChains> sm;
     for (int64_t gid = blockIdx.x; gid < nchunks; gid += gridDim.x) {
         if (!(ws.chunk_flag[gid] & kChunkRedo)) continue;  // uniform: one load per workgroup
-        chunk_hull<kLongNT, kLongP, kHullChains, WT>(y, w, n, m, sign, ws, full_slots, sm, gid);
+        chunk_hull<kLongNT, kLongP, kHullChains, WT, T>(y, w, n, m, sign, ws, full_slots, sm, gid);
         __syncthreads();
     }
 }
@@ -141,14 +142,14 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_redo(const float* __restrict_
 // Long rows, phase 3: every element takes the slope of the row-hull edge above
 // it (paper equation (3), section 3.4).
 // ----------------------------------------------------------------------------
-template <bool WT>
+template <bool WT, typename T>
 __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
-                                                   float* __restrict__ out,
+                                                   T* __restrict__ out,
                                                    int32_t* __restrict__ block_id, int rec_done) {
     constexpr int NT = kExpNT, C = kChunk;
     constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
     __shared__ int vidx[kExpTile + 1];
-    __shared__ float vslope[kExpTile + 1];
+    __shared__ T vslope[kExpTile + 1];
     __shared__ ChunkRec s_rc;
     __shared__ int s_inc, s_nan;
     const int64_t gid = blockIdx.x;
@@ -156,25 +157,30 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     const int j = (int)(gid - row * m);
     const int64_t off = row * n + (int64_t)j * C;
     const int len = (int)min((int64_t)C, n - (int64_t)j * C);
-    float* go = out + off;
+    const T sg = (T)sign;
+    T* go = out + off;
     int32_t* gb = block_id ? block_id + off : nullptr;
     const int tid = threadIdx.x;
     // element groups e = 4 * (g * NT + tid): consecutive threads write
-    // consecutive 16-byte groups
+    // consecutive groups of four
     const bool vec = ((((uintptr_t)go) | (uintptr_t)gb) & 15u) == 0;
-    auto store4 = [&](int e, float4 v, int4 b) {
+    auto store4 = [&](int e, const T (&v)[4], const int (&b)[4]) {
         if (vec && e + 4 <= len) {
             // streaming stores: the output is not read again here
-            typedef float f4v __attribute__((ext_vector_type(4)));
             typedef int i4v __attribute__((ext_vector_type(4)));
-            __builtin_nontemporal_store(f4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f4v*>(go + e));
-            if (gb) __builtin_nontemporal_store(i4v{b.x, b.y, b.z, b.w}, reinterpret_cast<i4v*>(gb + e));
+            if constexpr (sizeof(T) == 4) {
+                typedef float f4v __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4v*>(go + e));
+            } else {
+                typedef double d2v __attribute__((ext_vector_type(2)));
+                __builtin_nontemporal_store(d2v{v[0], v[1]}, reinterpret_cast<d2v*>(go + e));
+                __builtin_nontemporal_store(d2v{v[2], v[3]}, reinterpret_cast<d2v*>(go + e + 2));
+            }
+            if (gb) __builtin_nontemporal_store(i4v{b[0], b[1], b[2], b[3]}, reinterpret_cast<i4v*>(gb + e));
         } else {
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-            const int bb[4] = {b.x, b.y, b.z, b.w};
             for (int t = 0; t < 4 && e + t < len; ++t) {
-                go[e + t] = vv[t];
-                if (gb) gb[e + t] = bb[t];
+                go[e + t] = v[t];
+                if (gb) gb[e + t] = b[t];
             }
         }
     };
@@ -205,20 +211,24 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     }
     __syncthreads();
     if (s_nan) {
-        const float nan = __builtin_nanf("");
+        const T nan = (T)__builtin_nan("");
+        const T v4[4] = {nan, nan, nan, nan};
+        const int b4[4] = {-1, -1, -1, -1};
         for (int g = 0; g < G; ++g) {
             int e = 4 * (g * NT + tid);
-            if (e < len) store4(e, make_float4(nan, nan, nan, nan), make_int4(-1, -1, -1, -1));
+            if (e < len) store4(e, v4, b4);
         }
         return;
     }
     const ChunkRec rc = s_rc;
     if (rc.lo < 0) {
-        const float v = sign * (float)rc.slope_in;
+        const T v = sg * (T)rc.slope_in;
         const int b = rc.vb - 1;
+        const T v4[4] = {v, v, v, v};
+        const int b4[4] = {b, b, b, b};
         for (int g = 0; g < G; ++g) {
             int e = 4 * (g * NT + tid);
-            if (e < len) store4(e, make_float4(v, v, v, v), make_int4(b, b, b, b));
+            if (e < len) store4(e, v4, b4);
         }
         return;
     }
@@ -228,50 +238,54 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
         // between two surviving vertices is its own edge, so its fit is its
         // value; elements before or after the surviving range take the edges
         // into and out of it
-        const float* gy = ws.y + off;
+        const T* gy = static_cast<const T*>(ws.y) + off;
         const bool vy = vec && (((uintptr_t)gy) & 15u) == 0;
-        const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
+        const T sin_ = sg * (T)rc.slope_in, sout = sg * (T)rc.slope_out;
         // every load first, then the stores
-        float4 ya[G];
+        T ya[G][4];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
             if (vy && e0 + 4 <= len) {
-                typedef float f4v __attribute__((ext_vector_type(4)));
-                const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gy + e0));
-                ya[g] = make_float4(t.x, t.y, t.z, t.w);
+                if constexpr (sizeof(T) == 4) {
+                    typedef float f4v __attribute__((ext_vector_type(4)));
+                    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gy + e0));
+                    ya[g][0] = t.x; ya[g][1] = t.y; ya[g][2] = t.z; ya[g][3] = t.w;
+                } else {
+                    typedef double d2v __attribute__((ext_vector_type(2)));
+                    const d2v t0 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0));
+                    const d2v t1 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0 + 2));
+                    ya[g][0] = t0.x; ya[g][1] = t0.y; ya[g][2] = t1.x; ya[g][3] = t1.y;
+                }
             } else {
-                ya[g].x = e0 < len ? gy[e0] : 0.0f;
-                ya[g].y = e0 + 1 < len ? gy[e0 + 1] : 0.0f;
-                ya[g].z = e0 + 2 < len ? gy[e0 + 2] : 0.0f;
-                ya[g].w = e0 + 3 < len ? gy[e0 + 3] : 0.0f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) ya[g][t] = e0 + t < len ? gy[e0 + t] : T(0);
             }
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
             if (e0 >= len) break;
-            const float yy[4] = {ya[g].x, ya[g].y, ya[g].z, ya[g].w};
-            float vv[4];
+            T vv[4];
             int bb[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = e0 + t;
-                vv[t] = e < rc.lo ? sin_ : (e >= rc.hi ? sout : yy[t]);
+                vv[t] = e < rc.lo ? sin_ : (e >= rc.hi ? sout : ya[g][t]);
                 bb[t] = rc.vb + (e < rc.lo ? 0 : min(e - rc.lo + 1, nv)) - 1;
             }
-            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+            store4(e0, vv, bb);
         }
         return;
     }
     const size_t slot = (size_t)gid * (C + 1) + rc.lo;
-    const float sin_ = sign * (float)rc.slope_in, sout = sign * (float)rc.slope_out;
+    const T sin_ = sg * (T)rc.slope_in, sout = sg * (T)rc.slope_out;
     // the slope of edge (v, v+1) of the surviving vertices, from the slot
     auto edge_slope = [&](int v) {
         const double ds = ws.slot_S[slot + v + 1] - ws.slot_S[slot + v];
         const double dw = WT ? ws.slot_W[slot + v + 1] - ws.slot_W[slot + v]
                              : (double)((int)ws.slot_idx[slot + v + 1] - (int)ws.slot_idx[slot + v]);
-        return sign * (float)(ds / dw);
+        return sg * (T)(ds / dw);
     };
     if (nv <= kExpTile) {
         for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             const int e0 = 4 * (g * NT + tid);
             if (e0 >= len) break;
             int q = qg[g];
-            float vv[4];
+            T vv[4];
             int bb[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -304,7 +318,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
                 vv[t] = (q == 0) ? sin_ : (q == nv ? sout : vslope[q - 1]);
                 bb[t] = rc.vb + q - 1;
             }
-            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+            store4(e0, vv, bb);
         }
     } else {
         // many surviving vertices (a partly dense chunk): search the slot itself
@@ -319,8 +333,8 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
                 else hi = mid;
             }
             int q = lo, qs = -1;
-            float sl = 0.0f;
-            float vv[4];
+            T sl = T(0);
+            T vv[4];
             int bb[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -333,20 +347,20 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
                 vv[t] = (q == 0) ? sin_ : (q == nv ? sout : sl);
                 bb[t] = rc.vb + q - 1;
             }
-            store4(e0, make_float4(vv[0], vv[1], vv[2], vv[3]), make_int4(bb[0], bb[1], bb[2], bb[3]));
+            store4(e0, vv, bb);
         }
     }
 }
 
-template <int NT, int P>
-hipError_t launch_short_t(const float* y, const float* w, int64_t rows, int64_t n, float sign,
-                          float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {
+template <int NT, int P, typename T>
+hipError_t launch_short_t(const T* y, const T* w, int64_t rows, int64_t n, float sign, T* out,
+                          int32_t* block_id, int32_t* row_flag, hipStream_t st) {
     timed_begin(kPhaseShort, st);
     if (w)
-        hipLaunchKernelGGL((k_short_rows<NT, P, true>), dim3((unsigned)rows), dim3(NT), 0, st, y, w,
+        hipLaunchKernelGGL((k_short_rows<NT, P, true, T>), dim3((unsigned)rows), dim3(NT), 0, st, y, w,
                            n, sign, out, block_id, row_flag);
     else
-        hipLaunchKernelGGL((k_short_rows<NT, P, false>), dim3((unsigned)rows), dim3(NT), 0, st, y,
+        hipLaunchKernelGGL((k_short_rows<NT, P, false, T>), dim3((unsigned)rows), dim3(NT), 0, st, y,
                            w, n, sign, out, block_id, row_flag);
     timed_end(st);
     return hipGetLastError();
@@ -377,8 +391,9 @@ hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, 
     return hipGetLastError();
 }
 
-hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
-                        float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st) {
+template <typename T>
+hipError_t launch_short(const T* y, const T* w, int64_t rows, int64_t n, float sign, T* out,
+                        int32_t* block_id, int32_t* row_flag, hipStream_t st) {
     if (n <= 64) return launch_short_t<64, 1>(y, w, rows, n, sign, out, block_id, row_flag, st);
     if (n <= 128) return launch_short_t<64, 2>(y, w, rows, n, sign, out, block_id, row_flag, st);
     if (n <= 256) return launch_short_t<64, 4>(y, w, rows, n, sign, out, block_id, row_flag, st);
@@ -387,8 +402,9 @@ hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n,
     return launch_short_t<256, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
 }
 
-hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws0,
-                       float* out, int32_t* block_id, bool copy_control, hipStream_t st) {
+template <typename T>
+hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs& ws0, T* out,
+                       int32_t* block_id, bool copy_control, hipStream_t st) {
     const unsigned nblk = (unsigned)(sh.rows * sh.m);
     const bool wt = sh.weighted;
     LongWs ws = ws0;
@@ -396,27 +412,29 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
     ws.w = w;
     ws.n = sh.n;
     ws.sign = sh.sign;
+    ws.f64 = sizeof(T) == 8;
     // the copy control reads every chunk hull from its slot
     const int full_slots = copy_control ? 1 : 0;
     timed_begin(kPhaseChunk, st);
     if (wt)
-        hipLaunchKernelGGL(k_chunk_hulls<true>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+        hipLaunchKernelGGL((k_chunk_hulls<true, T>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
                            sh.sign, ws, full_slots);
     else
-        hipLaunchKernelGGL(k_chunk_hulls<false>, dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+        hipLaunchKernelGGL((k_chunk_hulls<false, T>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
                            sh.sign, ws, full_slots);
     timed_end(st);
     // chunks the chunk kernel gave up on are rebuilt by the first merge stage
-    // where the row takes the two-stage merge, else by the fallback kernel
-    if (copy_control || !two_stage_merge(sh.m)) {
+    // where the row takes the two-stage merge (f32 input), else by the
+    // fallback kernel
+    if (copy_control || !two_stage_merge(sh.m) || sizeof(T) == 8) {
         timed_begin(kPhaseChunkRedo, st);
         const unsigned nredo = nblk < kRedoGrid ? nblk : (unsigned)kRedoGrid;
         if (wt)
-            hipLaunchKernelGGL(k_chunk_redo<true>, dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
+            hipLaunchKernelGGL((k_chunk_redo<true, T>), dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
                                sh.sign, ws, full_slots, (int64_t)nblk);
         else
-            hipLaunchKernelGGL(k_chunk_redo<false>, dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
-                               sh.sign, ws, full_slots, (int64_t)nblk);
+            hipLaunchKernelGGL((k_chunk_redo<false, T>), dim3(nredo), dim3(kLongNT), 0, st, y, w, sh.n,
+                               sh.m, sh.sign, ws, full_slots, (int64_t)nblk);
         timed_end(st);
     }
     bool rec_done = true;
@@ -424,13 +442,22 @@ hipError_t launch_long(const float* y, const float* w, const LongShape& sh, cons
     if (e != hipSuccess) return e;
     timed_begin(kPhaseExpand, st);
     if (wt)
-        hipLaunchKernelGGL(k_expand<true>, dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign, ws,
+        hipLaunchKernelGGL((k_expand<true, T>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign, ws,
                            out, block_id, (int)rec_done);
     else
-        hipLaunchKernelGGL(k_expand<false>, dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign,
+        hipLaunchKernelGGL((k_expand<false, T>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign,
                            ws, out, block_id, (int)rec_done);
     timed_end(st);
     return hipGetLastError();
 }
+
+template hipError_t launch_short<float>(const float*, const float*, int64_t, int64_t, float, float*,
+                                        int32_t*, int32_t*, hipStream_t);
+template hipError_t launch_short<double>(const double*, const double*, int64_t, int64_t, float, double*,
+                                         int32_t*, int32_t*, hipStream_t);
+template hipError_t launch_long<float>(const float*, const float*, const LongShape&, const LongWs&, float*,
+                                       int32_t*, bool, hipStream_t);
+template hipError_t launch_long<double>(const double*, const double*, const LongShape&, const LongWs&,
+                                        double*, int32_t*, bool, hipStream_t);
 
 }  // namespace iso

@@ -111,11 +111,12 @@ struct LongWs {
     double* rslope;       // [R*m] slope of the root edge into each root segment (from the previous one)
     double* ck_S;         // [R*m*(kLongNT+1)] S at each thread's first point (and the chunk end)
     double* ck_W;         // (weighted only)
-    // the call's inputs, for points recomputed from them
-    const float* y;
-    const float* w;
+    // the call's inputs, for points recomputed from them and chunks rebuilt
+    const void* y;
+    const void* w;
     int64_t n;
     float sign;
+    int f64;              // y and w are f64 (else f32)
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
@@ -148,8 +149,10 @@ constexpr int kPhaseShort = 0, kPhaseChunk = 1, kPhaseMerge = 2, kPhaseExpand = 
 void timed_begin(int phase, hipStream_t st);
 void timed_end(hipStream_t st);
 
-hipError_t launch_short(const float* y, const float* w, int64_t rows, int64_t n, float sign,
-                        float* out, int32_t* block_id, int32_t* row_flag, hipStream_t st);
+// The fit of rows of at most kShortMax elements (T = float or double).
+template <typename T>
+hipError_t launch_short(const T* y, const T* w, int64_t rows, int64_t n, float sign, T* out,
+                        int32_t* block_id, int32_t* row_flag, hipStream_t st);
 
 // ORs the rows' data flags into *dst (one int) on the device, for the check.
 hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, hipStream_t st);
@@ -168,7 +171,9 @@ hipError_t launch_copy_merge(const LongShape& sh, const LongWs& ws, hipStream_t 
 // k_top_merge when there is more than one group).
 inline bool two_stage_merge(int m) { return (m + kGroup - 1) / kGroup <= kTopMax; }
 
-hipError_t launch_long(const float* y, const float* w, const LongShape& sh, const LongWs& ws,
-                       float* out, int32_t* block_id, bool copy_control, hipStream_t st);
+// The fit of long rows: chunk hulls, merge, expansion (T = float or double).
+template <typename T>
+hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs& ws, T* out,
+                       int32_t* block_id, bool copy_control, hipStream_t st);
 
 }  // namespace iso

@@ -288,7 +288,7 @@ struct GroupView {
     }
 };
 
-template <bool WT>
+template <bool WT, typename T>
 __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
     constexpr int NT = kGroupNT, G = kGroup, E = 2 * kWinK, EG = 2 * kGWinK;
     static_assert(G == 64, "one wave numbers a group's segments");
@@ -344,15 +344,18 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             redo = redo || h == 0;
         }
     }
-    if (__syncthreads_or(redo)) {
+    // (f64 input: the fallback kernel rebuilt them before this launch)
+    if (sizeof(T) == 4 && __syncthreads_or(redo)) {
         // chunks the chunk kernel gave up on (header h = 0, written in this
         // call): the whole workgroup rebuilds each with chains and merges,
         // then every window word is read again
         RedoSmem& hs = *reinterpret_cast<RedoSmem*>(pool);
         for (int i = 0; i < gc; ++i) {
             if (HC[i] != 0) continue;  // the same in every thread
-            chunk_hull<NT, kChunk / NT, kHullChains, WT>(ws.y, ws.w, ws.n, m, ws.sign, ws, 0, hs,
-                                                         rb + j0 + i);
+            if constexpr (sizeof(T) == 4)
+                chunk_hull<NT, kChunk / NT, kHullChains, WT, float>(static_cast<const float*>(ws.y),
+                                                                    static_cast<const float*>(ws.w), ws.n, m,
+                                                                    ws.sign, ws, 0, hs, rb + j0 + i);
             __syncthreads();
         }
         ok = true;
@@ -882,12 +885,14 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     if (two_stage_merge(sh.m)) {
         *rec_done = false;
         timed_begin(kPhaseMerge, st);
-        if (wt)
-            hipLaunchKernelGGL(k_group_merge<true>, dim3(R * (unsigned)ng), dim3(kGroupNT), 0, st, sh.m,
-                               ng, ws);
-        else
-            hipLaunchKernelGGL(k_group_merge<false>, dim3(R * (unsigned)ng), dim3(kGroupNT), 0, st, sh.m,
-                               ng, ws);
+        const dim3 grid(R * (unsigned)ng);
+        if (ws.f64) {
+            if (wt) hipLaunchKernelGGL((k_group_merge<true, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+            else hipLaunchKernelGGL((k_group_merge<false, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        } else {
+            if (wt) hipLaunchKernelGGL((k_group_merge<true, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+            else hipLaunchKernelGGL((k_group_merge<false, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        }
         timed_end(st);
         if (ng > 1) {
             const size_t lds = top_lds_bytes(ng, sh.m);

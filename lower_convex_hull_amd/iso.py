@@ -36,7 +36,8 @@ ISO_NOALLOC_BYTES = 64 << 20
 
 EXPORTS = ("iso_fit", "iso_fit_ex", "iso_fit_noalloc", "iso_workspace_bytes", "iso_status_str",
            "iso_release", "iso_chunk_size", "iso_short_row_max", "iso_timing_enable",
-           "iso_timing_read", "iso_vjp", "iso_vjp_f64", "iso_vjp_workspace_bytes")
+           "iso_timing_read", "iso_vjp", "iso_vjp_f64", "iso_vjp_workspace_bytes", "iso_fit_ex_f64",
+           "iso_fit_f64")
 
 _lib = None
 
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.iso_fit.restype = ctypes.c_int
         L.iso_fit_ex.argtypes = [p, p, i64, i64, p, p, p, sz, p, u32]
         L.iso_fit_ex.restype = ctypes.c_int
+        L.iso_fit_ex_f64.argtypes = [p, p, i64, i64, p, p, p, sz, p, u32]
+        L.iso_fit_ex_f64.restype = ctypes.c_int
+        L.iso_fit_f64.argtypes = [p, p, i64, i64, p]
+        L.iso_fit_f64.restype = ctypes.c_int
         L.iso_fit_noalloc.argtypes = [p, p, i64, i64, p, p, p, u32]
         L.iso_fit_noalloc.restype = ctypes.c_int
         L.iso_vjp.argtypes = [p, p, p, p, i64, i64, p, p, p, sz, p]
@@ -91,6 +96,16 @@ def iso_fit(y_ptr, w_ptr, rows, n, out_ptr) -> int:
 def iso_fit_ex(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes, stream, flags) -> int:
     return lib().iso_fit_ex(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes,
                             stream, flags)
+
+
+def iso_fit_ex_f64(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes, stream,
+                   flags) -> int:
+    return lib().iso_fit_ex_f64(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_bytes,
+                                stream, flags)
+
+
+def iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr) -> int:
+    return lib().iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr)
 
 
 def iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags) -> int:
@@ -165,28 +180,29 @@ def workspace(rows: int, n: int, weighted: bool, flags: int = 0, device=None):
 
 def fit(y, w=None, *, block_ids: bool = False, flags: int = 0, out=None, ws=None, stream=None,
         check: bool = True):
-    """Weighted isotonic fit of each row of a 2-D (or 1-D) float32 CUDA tensor.
+    """Weighted isotonic fit of each row of a 2-D (or 1-D) float32 or float64 CUDA tensor.
 
     Returns ``out`` (and ``block_id`` when ``block_ids``).  Raises IsoError on an
     error status; a NONFINITE warning is returned as NaN rows, not raised.
     """
     import torch
 
-    if y.dtype != torch.float32 or not y.is_cuda:
-        raise TypeError("y must be a float32 CUDA tensor")
+    if y.dtype not in (torch.float32, torch.float64) or not y.is_cuda:
+        raise TypeError("y must be a float32 or float64 CUDA tensor")
     y2 = y.reshape(1, -1) if y.dim() == 1 else y
     if not y2.is_contiguous():
         raise ValueError("y must be contiguous")
     rows, n = y2.shape
     if w is not None:
-        if w.dtype != torch.float32 or not w.is_cuda or w.numel() != y2.numel() or not w.is_contiguous():
-            raise ValueError("w must be a contiguous float32 CUDA tensor shaped like y")
+        if w.dtype != y.dtype or not w.is_cuda or w.numel() != y2.numel() or not w.is_contiguous():
+            raise ValueError("w must be a contiguous CUDA tensor of y's dtype, shaped like y")
     if out is None:
         out = torch.empty_like(y)
     bid = torch.empty(y.shape, dtype=torch.int32, device=y.device) if block_ids else None
     if ws is None:
         ws = workspace(rows, n, w is not None, flags, device=y.device)
-    st = iso_fit_ex(y2.data_ptr(), None if w is None else w.data_ptr(), rows, n, out.data_ptr(),
+    fn = iso_fit_ex if y.dtype == torch.float32 else iso_fit_ex_f64
+    st = fn(y2.data_ptr(), None if w is None else w.data_ptr(), rows, n, out.data_ptr(),
                     None if bid is None else bid.data_ptr(), ws.data_ptr(),
                     ws.numel() * ws.element_size(), _stream_handle(stream),
                     flags | (0 if check else ISO_F_NOCHECK))

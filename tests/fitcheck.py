@@ -184,3 +184,16 @@ def vjp_tolerance(y, w, g, bid, out_eps=2.0 ** -24):
     gw = d * r[rep]
     tol_gw = 2 * out_eps * np.abs(gw) + np.abs(d) * er[rep] + ez[rep] * (np.abs(r[rep]) + er[rep]) + 1e-300
     return tol_gy, tol_gw
+
+
+def parity_f64(y, w, out, z64, rel=1e-9):
+    """The f64 rule, per element: |out - z| <= rel (1 + |z|), z the oracle's f64 fit.
+    rel = 1e-9 reads the paper's f64 accuracy class (its float64 errors stay
+    within 1.3e-10 of 1 + |z*| on every family, section 7.6) with a margin for
+    a different summation order.  Returns (ok, worst ratio, row of worst)."""
+    out = np.atleast_2d(np.asarray(out, np.float64))
+    z64 = np.atleast_2d(np.asarray(z64, np.float64))
+    ratio = np.abs(out - z64) / (rel * (1.0 + np.abs(z64)))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    row = int(np.unravel_index(np.argmax(ratio), ratio.shape)[0]) if ratio.size else -1
+    return worst <= 1.0, worst, row
