@@ -48,6 +48,8 @@
  *                        iso_workspace_bytes() asks for, or the shape needs
  *                        more than iso_fit_noalloc's ISO_NOALLOC_BYTES.
  *                        Nothing launched.
+ *   ISO_ERR_DATA         iso_calib_fit got a non-finite score or outcome, or
+ *                        (with segments) a negative score or segment id.
  *   rows == 0 or n == 0 is a no-op that returns ISO_OK.
  *
  * The two warning/error statuses that depend on the data (NONFINITE, WEIGHT)
@@ -72,7 +74,8 @@ enum {
     ISO_ERR_WEIGHT = -2,
     ISO_ERR_NOMEM = -3,
     ISO_ERR_HIP = -4,
-    ISO_ERR_WORKSPACE = -5
+    ISO_ERR_WORKSPACE = -5,
+    ISO_ERR_DATA = -6
 };
 
 enum {
@@ -197,6 +200,48 @@ int iso_vjp_f64(const double* g, const double* y, const double* w, const int32_t
 /* Bytes of device workspace iso_vjp and iso_vjp_f64 need for this shape (0 for
  * rows of at most 2048 elements, or an empty or invalid shape). */
 size_t iso_vjp_workspace_bytes(int64_t rows, int64_t n);
+
+/*
+ * Calibration front end (paper section 7.7, "Case study: calibrating a click
+ * model"; the blog note's lab notebook, calibration cells), all f64.
+ *
+ * iso_calib_fit - an isotonic calibration curve from n scores and outcomes:
+ *   1. each score is keyed: the score itself, or with segments
+ *      segment[i] + min(score, 1 - 1e-12) (one curve per segment, all fitted
+ *      as one problem laid end to end);
+ *   2. the keys are sorted with their outcomes;
+ *   3. equal keys are pooled: xp[r] is the r-th distinct key, with the count
+ *      and the mean of the outcomes of its scores;
+ *   4. with segments, each mean is lifted by twice its segment index, so that
+ *      no block of the fit reaches across a segment boundary;
+ *   5. the means are fitted, the counts as weights, by the f64 fit;
+ *   6. the lift is dropped again: fp[r] is the curve at xp[r].
+ *   scores, outcomes [n] f64, device.  segment [n] int32 >= 0, device, or NULL.
+ *   xp, fp   [n] f64, device, written: the first *k_out entries are the curve.
+ *   k_out    host pointer: the number of distinct keys.
+ *   workspace device buffer of iso_calib_workspace_bytes(n) bytes, 256-byte
+ *            aligned, contents need no initialisation.
+ *   stream   hipStream_t (NULL = the null stream).
+ * The call waits for the GPU once (for the number of distinct keys).  Returns
+ * ISO_OK, ISO_ERR_ARG, ISO_ERR_DATA (non-finite score or outcome; with
+ * segments a negative score or segment id), ISO_ERR_WORKSPACE or ISO_ERR_HIP.
+ *
+ * iso_calib_apply - the curve (xp, fp) of k distinct keys at m new scores:
+ * the key of each score (as above; with segment != NULL the search stays in
+ * that segment's keys), linear interpolation between the two keys around it,
+ * held at the end values outside them.  A query whose segment has no keys, or
+ * whose score is NaN, gets NaN.  Only enqueues.  Returns ISO_OK, ISO_ERR_ARG
+ * or ISO_ERR_HIP.
+ *
+ * iso_calib_workspace_bytes - workspace of iso_calib_fit for n scores (0 for
+ * an invalid n); queries the current device's sort configuration.
+ */
+int iso_calib_fit(const double* scores, const double* outcomes, const int32_t* segment, int64_t n,
+                  double* xp, double* fp, int64_t* k_out, void* workspace, size_t workspace_bytes,
+                  void* stream);
+int iso_calib_apply(const double* xp, const double* fp, int64_t k, const double* scores,
+                    const int32_t* segment, int64_t m, double* out, void* stream);
+size_t iso_calib_workspace_bytes(int64_t n);
 
 /* Bytes of device workspace iso_fit_ex needs for this shape and these flags
  * (weighted or not is part of the shape: pass ISO_F_WEIGHTED_HINT in flags

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libiso.so")
-SOURCES = ["iso_api.hip", "iso_kernels.hip", "iso_merge.hip", "iso_copy.hip", "iso_vjp.hip"]
+SOURCES = ["iso_api.hip", "iso_kernels.hip", "iso_merge.hip", "iso_copy.hip", "iso_vjp.hip",
+           "iso_calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

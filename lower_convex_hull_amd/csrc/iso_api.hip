@@ -361,6 +361,7 @@ const char* iso_status_str(int status) {
         case ISO_ERR_NOMEM: return "device workspace allocation failed";
         case ISO_ERR_HIP: return "HIP runtime error";
         case ISO_ERR_WORKSPACE: return "workspace too small";
+        case ISO_ERR_DATA: return "non-finite score or outcome, or a negative score or segment";
         default: return "unknown status";
     }
 }

@@ -18,6 +18,9 @@ notebook):
   calibration, section 7.7; no records of any dataset are used).
 * ``family(name, n, seed)`` and ``weights(kind, n, seed)`` - the paper's
   accuracy families and weightings (section 7.6), synthetic.
+* ``click_scores(n, seed, segments)`` - unsorted f64 click-model scores with
+  recurring values, 0/1 clicks and optional segment ids, for the calibration
+  front end (section 7.7's shapes; no dataset records).
 """
 from __future__ import annotations
 
@@ -155,3 +158,28 @@ def consecutive_floats(n: int, start: float = 1.0) -> np.ndarray:
     """n consecutive float32 values upward from ``start``: every point its own block."""
     base = np.array([start], np.float32).view(np.int32)[0]
     return (base + np.arange(n, dtype=np.int64)).astype(np.int32).view(np.float32)
+
+
+def click_scores(n: int, seed: int, segments: int = 0, keep: float = 0.1):
+    """Synthetic stand-in for the paper's click-model calibration (section 7.7;
+    no records of its dataset are used): a model's predicted click
+    probabilities and the observed clicks, f64.
+
+    Scores are sigmoid(logit) of logits ~ N(-1.5, 1.2^2), rounded to float32
+    precision so that equal scores recur (as repeated feature vectors give
+    repeated scores).  The model is taken to have been trained with only a
+    fraction `keep` of the non-clicks, so its probabilities are too high; a
+    click is drawn with the probability keep*s / (keep*s + 1 - s).  With
+    `segments`, each score also gets a segment index in [0, segments) drawn
+    with probabilities proportional to 1/(j+1)^1.1 (a few large segments and a
+    long tail).  Returns (scores, clicks, segment or None)."""
+    rng = np.random.default_rng(seed)
+    logit = rng.normal(-1.5, 1.2, n)
+    s = (1.0 / (1.0 + np.exp(-logit))).astype(np.float32).astype(np.float64)
+    p = keep * s / (keep * s + 1.0 - s)
+    y = (rng.random(n) < p).astype(np.float64)
+    seg = None
+    if segments:
+        pr = 1.0 / np.arange(1, segments + 1) ** 1.1
+        seg = rng.choice(segments, size=n, p=pr / pr.sum()).astype(np.int32)
+    return s, y, seg

@@ -23,6 +23,7 @@ ISO_ERR_WEIGHT = -2
 ISO_ERR_NOMEM = -3
 ISO_ERR_HIP = -4
 ISO_ERR_WORKSPACE = -5
+ISO_ERR_DATA = -6
 
 ISO_F_NOCHECK = 1
 ISO_F_DECREASING = 2
@@ -37,7 +38,7 @@ ISO_NOALLOC_BYTES = 64 << 20
 EXPORTS = ("iso_fit", "iso_fit_ex", "iso_fit_noalloc", "iso_workspace_bytes", "iso_status_str",
            "iso_release", "iso_chunk_size", "iso_short_row_max", "iso_timing_enable",
            "iso_timing_read", "iso_vjp", "iso_vjp_f64", "iso_vjp_workspace_bytes", "iso_fit_ex_f64",
-           "iso_fit_f64")
+           "iso_fit_f64", "iso_calib_fit", "iso_calib_apply", "iso_calib_workspace_bytes")
 
 _lib = None
 
@@ -63,6 +64,12 @@ def lib() -> ctypes.CDLL:
         L.iso_fit_ex_f64.restype = ctypes.c_int
         L.iso_fit_f64.argtypes = [p, p, i64, i64, p]
         L.iso_fit_f64.restype = ctypes.c_int
+        L.iso_calib_fit.argtypes = [p, p, p, i64, p, p, p, p, sz, p]
+        L.iso_calib_fit.restype = ctypes.c_int
+        L.iso_calib_apply.argtypes = [p, p, i64, p, p, i64, p, p]
+        L.iso_calib_apply.restype = ctypes.c_int
+        L.iso_calib_workspace_bytes.argtypes = [i64]
+        L.iso_calib_workspace_bytes.restype = sz
         L.iso_fit_noalloc.argtypes = [p, p, i64, i64, p, p, p, u32]
         L.iso_fit_noalloc.restype = ctypes.c_int
         L.iso_vjp.argtypes = [p, p, p, p, i64, i64, p, p, p, sz, p]
@@ -106,6 +113,21 @@ def iso_fit_ex_f64(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_byte
 
 def iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr) -> int:
     return lib().iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr)
+
+
+def iso_calib_fit(scores_ptr, outcomes_ptr, segment_ptr, n, xp_ptr, fp_ptr, k_out, ws_ptr, ws_bytes,
+                  stream) -> int:
+    """k_out: a ctypes.c_int64 receiving the number of distinct keys."""
+    return lib().iso_calib_fit(scores_ptr, outcomes_ptr, segment_ptr, n, xp_ptr, fp_ptr,
+                               ctypes.byref(k_out), ws_ptr, ws_bytes, stream)
+
+
+def iso_calib_apply(xp_ptr, fp_ptr, k, scores_ptr, segment_ptr, m, out_ptr, stream) -> int:
+    return lib().iso_calib_apply(xp_ptr, fp_ptr, k, scores_ptr, segment_ptr, m, out_ptr, stream)
+
+
+def iso_calib_workspace_bytes(n) -> int:
+    return lib().iso_calib_workspace_bytes(n)
 
 
 def iso_fit_noalloc(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, stream, flags) -> int:
@@ -229,3 +251,22 @@ def vjp(g, y, w, block_id, *, grad_w: bool = False, stream=None):
     if st < 0:
         raise IsoError(st)
     return (gy, gw) if grad_w else gy
+
+
+def calib_curve(scores, outcomes, segment=None, stream=None):
+    """Calibration curve over torch CUDA f64 tensors: returns (xp, fp), each of
+    the number of distinct keys."""
+    import torch
+
+    n = scores.numel()
+    xp = torch.empty(n, dtype=torch.float64, device=scores.device)
+    fp = torch.empty_like(xp)
+    nb = iso_calib_workspace_bytes(n)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=scores.device)
+    k = ctypes.c_int64(0)
+    st = iso_calib_fit(scores.data_ptr(), outcomes.data_ptr(),
+                       None if segment is None else segment.data_ptr(), n, xp.data_ptr(),
+                       fp.data_ptr(), k, ws.data_ptr(), nb, _stream_handle(stream))
+    if st < 0:
+        raise IsoError(st)
+    return xp[:k.value], fp[:k.value]
