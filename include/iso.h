@@ -282,6 +282,12 @@ enum {
     ISO_PHASE_COUNT = 8
 };
 int iso_timing_enable(int on);
+
+/* Measurement probe: a plain streaming copy of `bytes` (a multiple of 16;
+ * src and dst 16-byte aligned device buffers that do not overlap) on `stream`,
+ * the practical HBM bandwidth ceiling the fit's kernels are measured against.
+ * Only enqueues.  Returns ISO_OK, ISO_ERR_ARG or ISO_ERR_HIP. */
+int iso_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 int iso_timing_read(double* ms, int64_t* launches, int nphase);
 
 #ifdef __cplusplus

@@ -319,6 +319,15 @@ void timed_end(hipStream_t st) {
 
 extern "C" {
 
+int iso_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
+    if (!src || !dst || bytes % 16 || (((uintptr_t)src | (uintptr_t)dst) & 15u)) return ISO_ERR_ARG;
+    if (overlaps(src, bytes, dst, bytes)) return ISO_ERR_ARG;
+    if (bytes == 0) return ISO_OK;
+    return iso::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ISO_OK
+               : ISO_ERR_HIP;
+}
+
 int iso_timing_enable(int on) {
     Timing& t = timing();
     std::lock_guard<std::mutex> lock(t.mu);

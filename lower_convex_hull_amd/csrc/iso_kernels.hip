@@ -384,7 +384,29 @@ __global__ __launch_bounds__(1024) void k_flags_or(const int32_t* __restrict__ f
     }
 }
 
+// A plain streaming copy (16 bytes per lane per step, grid-stride): the
+// practical HBM bandwidth ceiling the kernels are compared with.
+__global__ __launch_bounds__(256) void k_copy_probe(const float4* __restrict__ src, float4* __restrict__ dst,
+                                                    int64_t n16) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+        const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(src + i));
+        __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(dst + i));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t st) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int64_t g = (n16 + 255) / 256;
+    if (g > 256 * 64) g = 256 * 64;  // 64 workgroups per CU, grid-stride beyond
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL(k_copy_probe, dim3((unsigned)g), dim3(256), 0, st, static_cast<const float4*>(src),
+                       static_cast<float4*>(dst), n16);
+    return hipGetLastError();
+}
 
 hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, hipStream_t st) {
     hipLaunchKernelGGL(k_flags_or, dim3(1), dim3(1024), 0, st, row_flag, rows, dst);

@@ -154,6 +154,9 @@ template <typename T>
 hipError_t launch_short(const T* y, const T* w, int64_t rows, int64_t n, float sign, T* out,
                         int32_t* block_id, int32_t* row_flag, hipStream_t st);
 
+// The bandwidth probe: copies `bytes` (a multiple of 16, 16-byte aligned).
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t st);
+
 // ORs the rows' data flags into *dst (one int) on the device, for the check.
 hipError_t launch_flags_or(const int32_t* row_flag, int64_t rows, int32_t* dst, hipStream_t st);
 

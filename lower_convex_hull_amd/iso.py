@@ -38,7 +38,8 @@ ISO_NOALLOC_BYTES = 64 << 20
 EXPORTS = ("iso_fit", "iso_fit_ex", "iso_fit_noalloc", "iso_workspace_bytes", "iso_status_str",
            "iso_release", "iso_chunk_size", "iso_short_row_max", "iso_timing_enable",
            "iso_timing_read", "iso_vjp", "iso_vjp_f64", "iso_vjp_workspace_bytes", "iso_fit_ex_f64",
-           "iso_fit_f64", "iso_calib_fit", "iso_calib_apply", "iso_calib_workspace_bytes")
+           "iso_fit_f64", "iso_calib_fit", "iso_calib_apply", "iso_calib_workspace_bytes",
+           "iso_copy_probe")
 
 _lib = None
 
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.iso_fit_ex_f64.restype = ctypes.c_int
         L.iso_fit_f64.argtypes = [p, p, i64, i64, p]
         L.iso_fit_f64.restype = ctypes.c_int
+        L.iso_copy_probe.argtypes = [p, p, sz, p]
+        L.iso_copy_probe.restype = ctypes.c_int
         L.iso_calib_fit.argtypes = [p, p, p, i64, p, p, p, p, sz, p]
         L.iso_calib_fit.restype = ctypes.c_int
         L.iso_calib_apply.argtypes = [p, p, i64, p, p, i64, p, p]
@@ -113,6 +116,10 @@ def iso_fit_ex_f64(y_ptr, w_ptr, rows, n, out_ptr, block_id_ptr, ws_ptr, ws_byte
 
 def iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr) -> int:
     return lib().iso_fit_f64(y_ptr, w_ptr, rows, n, out_ptr)
+
+
+def iso_copy_probe(src_ptr, dst_ptr, nbytes, stream) -> int:
+    return lib().iso_copy_probe(src_ptr, dst_ptr, nbytes, stream)
 
 
 def iso_calib_fit(scores_ptr, outcomes_ptr, segment_ptr, n, xp_ptr, fp_ptr, k_out, ws_ptr, ws_bytes,
