@@ -446,9 +446,8 @@ hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs
                            sh.sign, ws, full_slots);
     timed_end(st);
     // chunks the chunk kernel gave up on are rebuilt by the first merge stage
-    // where the row takes the two-stage merge (f32 input), else by the
-    // fallback kernel
-    if (copy_control || !two_stage_merge(sh.m) || sizeof(T) == 8) {
+    // (f32 input), else (f64 input, the copy control) by the fallback kernel
+    if (copy_control || sizeof(T) == 8) {
         timed_begin(kPhaseChunkRedo, st);
         const unsigned nredo = nblk < kRedoGrid ? nblk : (unsigned)kRedoGrid;
         if (wt)

@@ -171,7 +171,8 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
 hipError_t launch_copy_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
 
 // Whether rows of m chunks take the two-stage merge (k_group_merge, then
-// k_top_merge when there is more than one group).
+// k_top_merge when there is more than one group); longer rows take
+// k_group_merge, then k_merge_rows.
 inline bool two_stage_merge(int m) { return (m + kGroup - 1) / kGroup <= kTopMax; }
 
 // The fit of long rows: chunk hulls, merge, expansion (T = float or double).

@@ -13,12 +13,13 @@
 namespace iso {
 namespace {
 
-// Rows beyond the two-stage merge: one workgroup per row runs every level of
-// the merge tree with the segment lists in the workspace.  Per level: one
-// thread per merge finds its bridge and cuts the two boundary segments in
-// place; then teams of threads move each right list's remaining descriptors
-// down behind the left list's (through a scratch copy, since the two ranges
-// may overlap).
+// Rows beyond the two-stage merge: after the first stage (k_group_merge, every
+// group of kGroup chunks merged in parallel, its list left at its first chunk's
+// slot), one workgroup per row runs the remaining levels of the merge tree with
+// the segment lists in the workspace.  Per level: one thread per merge finds its
+// bridge and cuts the two boundary segments in place; then teams of threads
+// move each right list's remaining descriptors down behind the left list's
+// (through a scratch copy, since the two ranges may overlap).
 template <bool WT>
 __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     constexpr int NT = kMergeNT;
@@ -62,11 +63,9 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
             carryW += tot;
         }
     }
-    for (int j = tid; j < m; j += NT) {
-        const int h = HC[j];
-        D[j] = mkdesc(j, 0, h - 1);
-        CNT[j] = 1;
-    }
+    // the first stage's group lists: their segment counts
+    const int ng = (m + kGroup - 1) / kGroup;
+    for (int g = tid; g < ng; g += NT) CNT[g * kGroup] = ws.gwin[row * ng + g].nseg;
     // warm this XCD's L2 with the compact hull ends of the whole row
     {
         const double2* wv = reinterpret_cast<const double2*>(ws.win + rb);
@@ -82,8 +81,8 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
               STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
 
-    // ---- the merge tree, level by level
-    for (int span = 1; span < m; span <<= 1) {
+    // ---- the merge tree's remaining levels
+    for (int span = kGroup; span < m; span <<= 1) {
         const int nm = (m - span + 2 * span - 1) / (2 * span);
         if (nm > NW) {
             // many merges: a thread each; walks that run long go to the waves
@@ -882,18 +881,19 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     const bool wt = sh.weighted;
     const int ng = (sh.m + kGroup - 1) / kGroup;
     const unsigned R = (unsigned)sh.rows;
+    // first stage: every group of kGroup chunks
+    timed_begin(kPhaseMerge, st);
+    const dim3 grid(R * (unsigned)ng);
+    if (ws.f64) {
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+    } else {
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+    }
+    timed_end(st);
     if (two_stage_merge(sh.m)) {
         *rec_done = false;
-        timed_begin(kPhaseMerge, st);
-        const dim3 grid(R * (unsigned)ng);
-        if (ws.f64) {
-            if (wt) hipLaunchKernelGGL((k_group_merge<true, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-            else hipLaunchKernelGGL((k_group_merge<false, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        } else {
-            if (wt) hipLaunchKernelGGL((k_group_merge<true, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-            else hipLaunchKernelGGL((k_group_merge<false, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        }
-        timed_end(st);
         if (ng > 1) {
             const size_t lds = top_lds_bytes(ng, sh.m);
             static std::once_flag attr_once;
@@ -913,10 +913,10 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
         }
         return hipGetLastError();
     }
-    // very long rows: one workgroup per row merges every level, lists in the
-    // workspace
+    // very long rows: one workgroup per row merges the group lists through the
+    // remaining levels, lists in the workspace
     *rec_done = true;
-    timed_begin(kPhaseMerge, st);
+    timed_begin(kPhaseMergeTop, st);
     if (wt)
         hipLaunchKernelGGL(k_merge_rows<true>, dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     else

@@ -231,6 +231,28 @@ def test_row_beyond_two_stage_merge(torch):
     check(torch, y, None, name="noisy/2.5e7", block_ids=False)
 
 
+def test_rows_of_1e8(torch):
+    """Rows of 10^8 elements (the paper's longest rows, Tables 1-3): beyond the
+    two-stage merge, the groups' lists are merged through the remaining levels
+    by one workgroup.  Noisy (against the oracle), consecutive floats (closed
+    form: the fit is the row, every element its own block), and consecutive
+    floats with cliffs so that bridges reach across groups at high levels."""
+    n = 100_000_000
+    y, _ = inputs.noisy(1, n, 81)
+    check(torch, y, None, name="noisy/1e8", block_ids=False)
+    del y
+    y = inputs.consecutive_floats(n)[None, :]
+    say("[parity] consecutive floats n=1e8")
+    st, out, bid = gpu_fit(torch, y)
+    assert st == 0 and np.array_equal(out, y)
+    assert np.array_equal(bid[0], np.arange(n, dtype=np.int32))
+    del out, bid
+    y = y.copy()
+    for c in (4096 * 64 * 3 + 5, 31_000_017, 77_777_777, n - 1):
+        y[0, c] = 0.5
+    check(torch, y, None, name="consecutive+cliffs/1e8", block_ids=False)
+
+
 def test_sawtooth_and_walk_families_at_1e6(torch):
     for fam in ("sawtooth", "random_walk", "cliff", "piecewise"):
         y = inputs.family(fam, 1_000_000, 24)[None, :]
