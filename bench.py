@@ -308,6 +308,61 @@ def extras(b, args, np):
     return out
 
 
+STAMP_PHASES = {
+    "chunk_hulls": ((0, 1, "loads, sums, scan"), (1, 5, "first quickhull level"), (5, 2, "later levels"),
+                    (2, 4, "slot and window writes"), (0, 4, "whole workgroup")),
+    "group_merge": ((0, 1, "prelude (window reads, starts)"), (1, 2, "merge tree"),
+                    (2, 3, "group list and window"), (3, 4, "descriptors out"), (0, 4, "whole workgroup")),
+    "top_merge": ((0, 1, "prelude (group windows, starts)"), (1, 2, "merge tree"),
+                  (2, 3, "root list and prefix"), (3, 4, "chunk starts, first segments"),
+                  (0, 4, "whole workgroup")),
+    "expand": ((0, 1, "record"), (1, 4, "stores"), (0, 4, "whole workgroup")),
+}
+
+
+def phase_stamps(b, y, calls=5):
+    """Per-phase durations inside the kernels of one long row (the library's
+    phase stamps: a 100 MHz counter read by thread 0 of each workgroup)."""
+    import numpy as np
+
+    torch, iso = b.torch, b.iso
+    R, N = y.shape
+    flags = iso.ISO_F_PHASE_STAMPS
+    nb0 = iso.iso_workspace_bytes(R, N, 0)
+    nb = iso.iso_workspace_bytes(R, N, flags)
+    m = -(-N // iso.iso_chunk_size(N))
+    ng = -(-m // 64)
+    ws = torch.empty(nb, dtype=torch.uint8, device=b.dev)
+    out = torch.empty_like(y)
+    acc = {}
+    for _ in range(calls):
+        b.flush()
+        ws[nb0:].zero_()
+        assert iso.iso_fit_ex(y.data_ptr(), None, R, N, out.data_ptr(), None, ws.data_ptr(), nb, b.sh,
+                              flags | iso.ISO_F_NOCHECK) == 0
+        b.stream.synchronize()
+        st = ws[nb0:nb0 + (2 * R * m + R * ng + R) * 64].view(torch.int64).cpu().numpy().reshape(-1, 8)
+        parts = {"chunk_hulls": st[:R * m], "group_merge": st[R * m:R * m + R * ng],
+                 "top_merge": st[R * m + R * ng:R * m + R * ng + R],
+                 "expand": st[R * m + R * ng + R:]}
+        for kname, arr in parts.items():
+            arr = arr[arr[:, 0] > 0]
+            if not len(arr):
+                continue
+            d = acc.setdefault(kname, {"span_us": [], "wg": len(arr)})
+            d["span_us"].append((arr[:, 4].max() - arr[:, 0].min()) / 100.0)
+            for a, z, name in STAMP_PHASES[kname]:
+                ok = (arr[:, a] > 0) & (arr[:, z] > 0)
+                if ok.any():
+                    d.setdefault(name, []).append(float(np.median(arr[ok, z] - arr[ok, a])) / 100.0)
+    res = {}
+    for kname, d in acc.items():
+        res[kname] = {"workgroups": d["wg"], "launch_span_us": round(float(np.median(d["span_us"])), 2),
+                      "median_per_workgroup_us": {k: round(float(np.median(v)), 2) for k, v in d.items()
+                                                  if k not in ("span_us", "wg")}}
+    return res
+
+
 def copy_ceiling(b, K):
     """The library's streaming copy kernel, cache flushed before each call."""
     torch, iso = b.torch, b.iso
@@ -441,6 +496,7 @@ def main():
             }
             del seg_job, cpy_job, yt
         rep_extra["merge_control"] = ctl
+        rep_extra["phase_stamps"] = {j.label: phase_stamps(b, j.keep[0]) for j in jobs}
         rep_extra["workloads"] = extras(b, args, np)
 
     # ---- CPU oracle baseline (bounded sample of the same rows)

@@ -92,7 +92,19 @@ enum {
     ISO_F_COPY_CONTROL = 4u,
     /* For iso_workspace_bytes only: size the workspace for a weighted call
      * (w != NULL).  Ignored by the fitting calls. */
-    ISO_F_WEIGHTED_HINT = 0x100u
+    ISO_F_WEIGHTED_HINT = 0x100u,
+    /* Measurement: on long rows, thread 0 of every workgroup of the chunk,
+     * first-merge-stage, second-merge-stage and expansion kernels records the
+     * device's 100 MHz real-time counter at its phase boundaries.  The stamps
+     * take 64 bytes per workgroup at the end of the workspace (pass the flag to
+     * iso_workspace_bytes too), from byte iso_workspace_bytes(rows, n, flags
+     * without this bit) on: rows*m rows of 8 uint64 for the chunk kernel, then
+     * rows*ng for the first merge stage (ng = ceil(m / 64)), rows for the
+     * second stage, rows*m for the expansion (m = ceil(n / iso_chunk_size(n))).
+     * Slots: chunk 0 start, 1 loads/sums/scan, 5 first quickhull level, 2 hull
+     * built, 4 end; merge stages 0 start, 1 prelude, 2 merge tree, 3 lists and
+     * windows written, 4 end; expansion 0 start, 1 record ready, 4 end. */
+    ISO_F_PHASE_STAMPS = 0x200u
 };
 
 /*

@@ -29,11 +29,12 @@ struct Plan {
     size_t off_slot_idx = 0, off_slot_S = 0, off_slot_W = 0, off_st_S = 0, off_st_W = 0, off_win = 0;
     size_t off_desc = 0, off_node_cnt = 0, off_vb = 0, off_rec = 0, off_desc_scr = 0, off_mi = 0;
     size_t off_gwin = 0, off_gtot = 0, off_cst = 0, off_gpre = 0, off_root_n = 0, off_ck_S = 0, off_ck_W = 0, off_rslope = 0;
+    size_t off_stamps = 0;  // phase stamps (ISO_F_PHASE_STAMPS), at the end
     size_t off_cp_a = 0, off_cp_b = 0, off_cp_off = 0, off_cp_cnt = 0, off_cp_off2 = 0,
            off_cp_cnt2 = 0, off_cp_cut = 0, off_cp_cut2 = 0;
 };
 
-bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
+bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p, bool stamps = false) {
     *p = Plan();
     if (rows < 0 || n < 0) return false;
     if (rows == 0 || n == 0) return true;
@@ -95,6 +96,7 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p) {
         p->off_cp_cut = take(M * sizeof(int32_t));
         p->off_cp_cut2 = take(M * sizeof(int32_t));
     }
+    if (stamps) p->off_stamps = take((2 * M + NG + R) * iso::kStampSlots * sizeof(uint64_t));
     p->bytes = at;
     return true;
 }
@@ -104,8 +106,16 @@ T* at(void* base, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
-iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control) {
+iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control, int64_t rows) {
     iso::LongWs ws{};
+    if (p.off_stamps) {
+        const int64_t M = rows * p.m, NG = rows * ((p.m + iso::kGroup - 1) / iso::kGroup);
+        uint64_t* s0 = at<uint64_t>(base, p.off_stamps);
+        ws.st_chunk = s0;
+        ws.st_group = s0 + M * iso::kStampSlots;
+        ws.st_top = ws.st_group + NG * iso::kStampSlots;
+        ws.st_expand = ws.st_top + rows * iso::kStampSlots;
+    }
     ws.chunk_flag = at<int32_t>(base, p.off_chunk_flag);
     ws.tot_S = at<double>(base, p.off_tot_S);
     ws.tot_W = weighted ? at<double>(base, p.off_tot_W) : nullptr;
@@ -151,7 +161,7 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 }
 
 constexpr uint32_t kKnownFlags =
-    ISO_F_NOCHECK | ISO_F_DECREASING | ISO_F_COPY_CONTROL | ISO_F_WEIGHTED_HINT;
+    ISO_F_NOCHECK | ISO_F_DECREASING | ISO_F_COPY_CONTROL | ISO_F_WEIGHTED_HINT | ISO_F_PHASE_STAMPS;
 
 // Launch timing (benchmarks only).
 struct Timing {
@@ -191,7 +201,7 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
     const bool weighted = w != nullptr;
     const bool copy_control = (flags & ISO_F_COPY_CONTROL) != 0;
     Plan p;
-    if (!plan(rows, n, weighted, copy_control, &p)) return ISO_ERR_ARG;
+    if (!plan(rows, n, weighted, copy_control, &p, (flags & ISO_F_PHASE_STAMPS) != 0)) return ISO_ERR_ARG;
     const size_t nb = (size_t)rows * (size_t)n * sizeof(T);
     const size_t ib = (size_t)rows * (size_t)n * sizeof(int32_t);
     if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, ib, y, nb) ||
@@ -210,7 +220,7 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
         e = iso::launch_short<T>(y, w, rows, n, sign, out, block_id, row_flag, st);
     } else {
         iso::LongShape sh{rows, n, p.m, weighted, sign};
-        iso::LongWs ws = long_ws(workspace, p, weighted, copy_control);
+        iso::LongWs ws = long_ws(workspace, p, weighted, copy_control, rows);
         e = iso::launch_long<T>(y, w, sh, ws, out, block_id, copy_control, st);
     }
     if (e != hipSuccess) return ISO_ERR_HIP;
@@ -380,7 +390,8 @@ int64_t iso_short_row_max(void) { return iso::kShortMax; }
 
 size_t iso_workspace_bytes(int64_t rows, int64_t n, uint32_t flags) {
     Plan p;
-    if (!plan(rows, n, (flags & ISO_F_WEIGHTED_HINT) != 0, (flags & ISO_F_COPY_CONTROL) != 0, &p))
+    if (!plan(rows, n, (flags & ISO_F_WEIGHTED_HINT) != 0, (flags & ISO_F_COPY_CONTROL) != 0, &p,
+              (flags & ISO_F_PHASE_STAMPS) != 0))
         return 0;
     return p.bytes;
 }

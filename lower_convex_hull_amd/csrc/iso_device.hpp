@@ -12,6 +12,15 @@ struct Pt {
     double s;
 };
 
+// Phase stamp (measurement only): thread 0 of the workgroup records the
+// 100 MHz real-time counter in slot k of its row of stamps, if there is one.
+__device__ __forceinline__ void stamp(uint64_t* row, int k) {
+    if (row && threadIdx.x == 0) row[k] = (uint64_t)wall_clock64();
+}
+__device__ __forceinline__ uint64_t* stamp_row(uint64_t* area, int64_t wg) {
+    return area ? area + wg * kStampSlots : nullptr;
+}
+
 // z-component of (b - a) x (c - a).  For a, b, c in increasing abscissa, > 0
 // means b lies strictly below the chord from a to c (a strict left turn), so b
 // is a hull vertex of {a, b, c}; <= 0 means b is on or above the chord and is

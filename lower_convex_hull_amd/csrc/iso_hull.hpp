@@ -133,7 +133,8 @@ __device__ __forceinline__ void load_elems(const T* __restrict__ p, T (&v)[P]) {
 template <int NT, int P, bool WT, int MODE, typename T>
 __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, const T* __restrict__ gy,
                               const T* __restrict__ gw, int len, float sign, T (&yv)[P],
-                              double (&ps)[P], double (&pw)[P], double& s0, double& w0) {
+                              double (&ps)[P], double (&pw)[P], double& s0, double& w0,
+                              uint64_t* sr = nullptr /* phase stamps */) {
     constexpr int RS = P + 1;
     const int L = threadIdx.x;
     const int base = L * P;
@@ -252,6 +253,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             if (base + b < len) inc = inc && yv[b - 1] < yv[b];
     }
     const bool all = __syncthreads_and(inc) != 0;  // also publishes end_s, end_w
+    stamp(sr, 1);  // loads, sums, scan and the increasing test done
     if (!full && base + P > len) {
         const double es = sm.end_s, ew = sm.end_w;
         if (base >= len) { s0 = es; w0 = ew; }
@@ -461,6 +463,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             nv += add;
             cb = 1 - cb;
             __syncthreads();
+            if (lv == 0) stamp(sr, 5);  // first quickhull level done
         }
         if (state == 1) {
             // the vertex list, made convex as computed (a near-tie may have
@@ -658,7 +661,8 @@ template <int NT, int P, int MODE, bool WT, typename T>
 __device__ __forceinline__ void chunk_hull(const T* __restrict__ y, const T* __restrict__ w,
                                            int64_t n, int m, float sign, const LongWs& ws,
                                            int full_slots, HullSmem<NT, P, WT, MODE>& sm,
-                                           int64_t gid /* row * m + chunk */) {
+                                           int64_t gid /* row * m + chunk */,
+                                           uint64_t* sr = nullptr /* phase stamps */) {
     constexpr int C = kChunk;
     static_assert(NT * P == C, "a workgroup covers one chunk");
     const int64_t row = gid / m;
@@ -668,7 +672,8 @@ __device__ __forceinline__ void chunk_hull(const T* __restrict__ y, const T* __r
     T yv[P];
     double ps[P], pw[P], s0, w0;
     const HullOut ho = block_hull<NT, P, WT, MODE, T>(sm, y + off, WT ? w + off : nullptr, len, sign, yv,
-                                                   ps, pw, s0, w0);
+                                                   ps, pw, s0, w0, sr);
+    stamp(sr, 2);  // hull built
     const int L = threadIdx.x;
     const int base = L * P;
     const int h = ho.h;

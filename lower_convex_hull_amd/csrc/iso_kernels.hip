@@ -119,7 +119,10 @@ __global__ __launch_bounds__(kLongNT, WT || sizeof(T) == 8 ? 2 : 4) void k_chunk
     const T* __restrict__ y, const T* __restrict__ w, int64_t n, int m, float sign, LongWs ws,
     int full_slots) {
     __shared__ HullSmem<kLongNT, kLongP, WT, kHullQuick> sm;
-    chunk_hull<kLongNT, kLongP, kHullQuick, WT, T>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x);
+    uint64_t* const sr = stamp_row(ws.st_chunk, blockIdx.x);
+    stamp(sr, 0);
+    chunk_hull<kLongNT, kLongP, kHullQuick, WT, T>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x, sr);
+    stamp(sr, 4);  // end
 }
 
 // The fallback for rows the first merge stage does not take (rows beyond the
@@ -161,6 +164,8 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     T* go = out + off;
     int32_t* gb = block_id ? block_id + off : nullptr;
     const int tid = threadIdx.x;
+    uint64_t* const sr = stamp_row(ws.st_expand, gid);
+    stamp(sr, 0);
     // element groups e = 4 * (g * NT + tid): consecutive threads write
     // consecutive groups of four
     const bool vec = ((((uintptr_t)go) | (uintptr_t)gb) & 15u) == 0;
@@ -210,6 +215,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
         s_nan = (rf & kFlagNonfinite) != 0;
     }
     __syncthreads();
+    stamp(sr, 1);  // record ready
     if (s_nan) {
         const T nan = (T)__builtin_nan("");
         const T v4[4] = {nan, nan, nan, nan};
@@ -218,6 +224,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             int e = 4 * (g * NT + tid);
             if (e < len) store4(e, v4, b4);
         }
+        stamp(sr, 4);
         return;
     }
     const ChunkRec rc = s_rc;
@@ -230,6 +237,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             int e = 4 * (g * NT + tid);
             if (e < len) store4(e, v4, b4);
         }
+        stamp(sr, 4);
         return;
     }
     const int nv = rc.hi - rc.lo + 1;
@@ -276,6 +284,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             }
             store4(e0, vv, bb);
         }
+        stamp(sr, 4);
         return;
     }
     const size_t slot = (size_t)gid * (C + 1) + rc.lo;
@@ -350,6 +359,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             store4(e0, vv, bb);
         }
     }
+    stamp(sr, 4);  // end
 }
 
 template <int NT, int P, typename T>

@@ -32,6 +32,9 @@ constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed 
 constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
 constexpr int kHardCap = 256;     // merges per level a wave may take over
 
+// Phase stamps per workgroup (ISO_F_PHASE_STAMPS).
+constexpr int kStampSlots = 8;
+
 // Per-row data flags written by the kernels (read back by the checking path).
 constexpr int kFlagNonfinite = 1;
 constexpr int kFlagWeight = 2;
@@ -120,6 +123,12 @@ struct LongWs {
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
+    // phase stamps (measurement only, null unless ISO_F_PHASE_STAMPS): per
+    // workgroup kStampSlots 100 MHz real-time counter values
+    uint64_t* st_chunk;   // [R*m]  chunk kernel
+    uint64_t* st_group;   // [R*ng] first merge stage
+    uint64_t* st_top;     // [R]    second merge stage (or the row merge)
+    uint64_t* st_expand;  // [R*m]  expansion
     // grid-copy control only
     void* cp_a;           // [R*m*(C+1)] flat vertex buffers (ping), 16 B (24 B weighted) each
     void* cp_b;           // (pong)

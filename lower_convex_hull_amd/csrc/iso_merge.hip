@@ -34,6 +34,8 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     const int tid = threadIdx.x;
     const int wid = tid >> 6, wlane = tid & 63;
 
+    uint64_t* const sr = stamp_row(ws.st_top, row);
+    stamp(sr, 0);
     uint2* const D = ws.desc + rb;
     uint2* const SCR = ws.desc_scr + rb;
     int32_t* const CNT = ws.node_cnt + rb;
@@ -152,8 +154,10 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
         __syncthreads();
     }
 
+    stamp(sr, 2);  // merge tree done
     // ---- reconstruction records (Corollary 4.5)
     write_records<NT>(X, D, CNT[0], m, ws.vb + rb, ws.rec + rb, ired);
+    stamp(sr, 4);  // end
 }
 
 
@@ -313,6 +317,8 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     const int64_t rb = row * m;
     const int j0 = g * G, gc = min(G, m - j0);
     const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
+    uint64_t* const sr = stamp_row(ws.st_group, gid);
+    stamp(sr, 0);
 
     // the prelude's global reads, issued together: every chunk window (raw
     // 16-byte words, the hull count in each header) and the chunk totals
@@ -389,6 +395,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         if (wlane == 0) ws.gtot[row * ng + g] = make_double2(totS, WT ? totW : 0.0);
     }
     const bool fast = __syncthreads_and(ok) != 0;
+    stamp(sr, 1);  // prelude loaded (and any rebuilt chunks), starts scanned
     const size_t sl = (size_t)(rb + j0) * (kChunk + 1);
     GroupWin* gwo = ws.gwin + row * ng + g;
     int nseg, hg;
@@ -414,6 +421,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         }
         __syncthreads();
         merge_arrays<NT>(ar, CNT, VER, gc, E);
+        stamp(sr, 2);  // merge tree done (compact arrays)
         hg = CNT[0];
         // the group's list: one segment per run of a chunk's vertices
         for (int t = tid; t < hg; t += NT) {
@@ -477,6 +485,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             for (int span = 1; span < gc; span <<= 1)
                 merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
         }
+        stamp(sr, 2);  // merge tree done (segment lists)
         nseg = CNT[0];
         if (wid == 0) {
             int v = 0;
@@ -508,6 +517,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             gwo->tag[t] = mktag(j0 + dchunk(d), pos);
         }
     }
+    stamp(sr, 3);  // group window written
     for (int i = tid; i < nseg; i += NT) {
         const uint2 d = D[i];
         ws.desc[rb + j0 + i] = mkdesc(j0 + dchunk(d), dlo(d), dhi(d));
@@ -554,6 +564,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             ws.root_n[row] = nseg | (fast ? kRootSlopes : 0);
         }
     }
+    stamp(sr, 4);  // end
 }
 
 // Dynamic LDS of the second stage: group starts gS, gW (8 B each), then
@@ -582,6 +593,8 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m, gb = row * ng;
     const int tid = threadIdx.x;
+    uint64_t* const sr = stamp_row(ws.st_top, row);
+    stamp(sr, 0);
 
     // the prelude's global reads, issued together: every group window (raw
     // 16-byte words; the header holds the hull count, segment count and data
@@ -649,6 +662,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         }
     }
     const bool fast = (__syncthreads_and(ok) != 0) && ng <= kTopFastMax && m < kTagMaxChunks;
+    stamp(sr, 1);  // prelude loaded, group starts scanned
     uint2* R = ws.desc_scr + rb;  // the root list, as segments of chunk hulls
     // after both paths' LDS: the root segments' chunks (and, on the compact
     // path, their vertex prefix), for the record prefix counts
@@ -687,6 +701,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         }
         __syncthreads();
         merge_arrays<NT>(ar, CNT, s_ver, ng, E);
+        stamp(sr, 2);  // merge tree done (compact arrays)
         const int hr = CNT[0];
         // one root segment per run of a chunk's vertices; its chunk into rcbuf
         uint16_t* R16 = reinterpret_cast<uint16_t*>(R);
@@ -757,6 +772,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             for (int span = 1; span < ng; span <<= 1)
                 merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
         }
+        stamp(sr, 2);  // merge tree done (segment lists)
 
         // the root list over groups, expanded into segments of chunk hulls:
         // first the range of group-list segments each root entry covers, then
@@ -848,6 +864,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             x += len[q];
         }
     }
+    stamp(sr, 3);  // root list and its vertex prefix written
     // chunk starts of the row: group start plus the chunk's start in its group
 #pragma unroll
     for (int q = 0; q < kRo; ++q) {
@@ -871,6 +888,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         ws.row_flag[row] = f;
         ws.root_n[row] = nroot | (fast ? kRootSlopes : 0);
     }
+    stamp(sr, 4);  // end (chunk starts and each chunk's first root segment written)
 }
 
 }  // namespace

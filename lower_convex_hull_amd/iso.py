@@ -29,6 +29,7 @@ ISO_F_NOCHECK = 1
 ISO_F_DECREASING = 2
 ISO_F_COPY_CONTROL = 4
 ISO_F_WEIGHTED_HINT = 0x100
+ISO_F_PHASE_STAMPS = 0x200
 
 ISO_PHASE_NAMES = ("short_rows", "chunk_hulls", "merge", "expand", "copy_bridge", "copy_move",
                    "merge_top", "chunk_redo")
