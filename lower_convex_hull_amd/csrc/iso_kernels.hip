@@ -114,12 +114,12 @@ __global__ __launch_bounds__(NT) void k_short_rows(const T* __restrict__ y,
 }
 
 
-template <bool WT, typename T>
+template <bool WT, typename T, bool ST>
 __global__ __launch_bounds__(kLongNT, WT || sizeof(T) == 8 ? 2 : 4) void k_chunk_hulls(
     const T* __restrict__ y, const T* __restrict__ w, int64_t n, int m, float sign, LongWs ws,
     int full_slots) {
     __shared__ HullSmem<kLongNT, kLongP, WT, kHullQuick> sm;
-    uint64_t* const sr = stamp_row(ws.st_chunk, blockIdx.x);
+    uint64_t* const sr = ST ? stamp_row(ws.st_chunk, blockIdx.x) : nullptr;
     stamp(sr, 0);
     chunk_hull<kLongNT, kLongP, kHullQuick, WT, T>(y, w, n, m, sign, ws, full_slots, sm, blockIdx.x, sr);
     stamp(sr, 4);  // end
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_redo(const T* __restrict__ y,
 // Long rows, phase 3: every element takes the slope of the row-hull edge above
 // it (paper equation (3), section 3.4).
 // ----------------------------------------------------------------------------
-template <bool WT, typename T>
+template <bool WT, typename T, bool ST>
 __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign, LongWs ws,
                                                    T* __restrict__ out,
                                                    int32_t* __restrict__ block_id, int rec_done) {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     T* go = out + off;
     int32_t* gb = block_id ? block_id + off : nullptr;
     const int tid = threadIdx.x;
-    uint64_t* const sr = stamp_row(ws.st_expand, gid);
+    uint64_t* const sr = ST ? stamp_row(ws.st_expand, gid) : nullptr;
     stamp(sr, 0);
     // element groups e = 4 * (g * NT + tid): consecutive threads write
     // consecutive groups of four
@@ -447,13 +447,25 @@ hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs
     ws.f64 = sizeof(T) == 8;
     // the copy control reads every chunk hull from its slot
     const int full_slots = copy_control ? 1 : 0;
+    // phase stamps (measurement only) come from separate instances of the
+    // kernels, so that the others carry no stamp code
+    const bool stamps = ws.st_chunk != nullptr && sizeof(T) == 4;
     timed_begin(kPhaseChunk, st);
-    if (wt)
-        hipLaunchKernelGGL((k_chunk_hulls<true, T>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
-                           sh.sign, ws, full_slots);
-    else
-        hipLaunchKernelGGL((k_chunk_hulls<false, T>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n, sh.m,
-                           sh.sign, ws, full_slots);
+    if (stamps) {
+        if (wt)
+            hipLaunchKernelGGL((k_chunk_hulls<true, T, true>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n,
+                               sh.m, sh.sign, ws, full_slots);
+        else
+            hipLaunchKernelGGL((k_chunk_hulls<false, T, true>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n,
+                               sh.m, sh.sign, ws, full_slots);
+    } else {
+        if (wt)
+            hipLaunchKernelGGL((k_chunk_hulls<true, T, false>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n,
+                               sh.m, sh.sign, ws, full_slots);
+        else
+            hipLaunchKernelGGL((k_chunk_hulls<false, T, false>), dim3(nblk), dim3(kLongNT), 0, st, y, w, sh.n,
+                               sh.m, sh.sign, ws, full_slots);
+    }
     timed_end(st);
     // chunks the chunk kernel gave up on are rebuilt by the first merge stage
     // (f32 input), else (f64 input, the copy control) by the fallback kernel
@@ -472,12 +484,21 @@ hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs
     hipError_t e = copy_control ? launch_copy_merge(sh, ws, st) : launch_segment_merge(sh, ws, st, &rec_done);
     if (e != hipSuccess) return e;
     timed_begin(kPhaseExpand, st);
-    if (wt)
-        hipLaunchKernelGGL((k_expand<true, T>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign, ws,
-                           out, block_id, (int)rec_done);
-    else
-        hipLaunchKernelGGL((k_expand<false, T>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign,
-                           ws, out, block_id, (int)rec_done);
+    if (stamps) {
+        if (wt)
+            hipLaunchKernelGGL((k_expand<true, T, true>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m, sh.sign,
+                               ws, out, block_id, (int)rec_done);
+        else
+            hipLaunchKernelGGL((k_expand<false, T, true>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m,
+                               sh.sign, ws, out, block_id, (int)rec_done);
+    } else {
+        if (wt)
+            hipLaunchKernelGGL((k_expand<true, T, false>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m,
+                               sh.sign, ws, out, block_id, (int)rec_done);
+        else
+            hipLaunchKernelGGL((k_expand<false, T, false>), dim3(nblk), dim3(kExpNT), 0, st, sh.n, sh.m,
+                               sh.sign, ws, out, block_id, (int)rec_done);
+    }
     timed_end(st);
     return hipGetLastError();
 }

@@ -20,7 +20,7 @@ namespace {
 // bridge and cuts the two boundary segments in place; then teams of threads
 // move each right list's remaining descriptors down behind the left list's
 // (through a scratch copy, since the two ranges may overlap).
-template <bool WT>
+template <bool WT, bool ST>
 __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     constexpr int NT = kMergeNT;
     __shared__ double red[NT / 64 + 1];
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     const int tid = threadIdx.x;
     const int wid = tid >> 6, wlane = tid & 63;
 
-    uint64_t* const sr = stamp_row(ws.st_top, row);
+    uint64_t* const sr = ST ? stamp_row(ws.st_top, row) : nullptr;
     stamp(sr, 0);
     uint2* const D = ws.desc + rb;
     uint2* const SCR = ws.desc_scr + rb;
@@ -291,7 +291,7 @@ struct GroupView {
     }
 };
 
-template <bool WT, typename T>
+template <bool WT, typename T, bool ST>
 __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
     constexpr int NT = kGroupNT, G = kGroup, E = 2 * kWinK, EG = 2 * kGWinK;
     static_assert(G == 64, "one wave numbers a group's segments");
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     const int64_t rb = row * m;
     const int j0 = g * G, gc = min(G, m - j0);
     const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
-    uint64_t* const sr = stamp_row(ws.st_group, gid);
+    uint64_t* const sr = ST ? stamp_row(ws.st_group, gid) : nullptr;
     stamp(sr, 0);
 
     // the prelude's global reads, issued together: every chunk window (raw
@@ -580,7 +580,7 @@ __host__ __device__ inline size_t top_lds_main(int ng) {
 __host__ __device__ inline int top_root_cap(int ng, int m) { return m < ng * 2 * kGWinK ? m : ng * 2 * kGWinK; }
 inline size_t top_lds_bytes(int ng, int m) { return top_lds_main(ng) + (size_t)top_root_cap(ng, m) * 4; }
 
-template <bool WT>
+template <bool WT, bool ST>
 __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
     constexpr int NT = kTopNT, G = kGroup, E = 2 * kGWinK;
     extern __shared__ int4 top_lds[];
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m, gb = row * ng;
     const int tid = threadIdx.x;
-    uint64_t* const sr = stamp_row(ws.st_top, row);
+    uint64_t* const sr = ST ? stamp_row(ws.st_top, row) : nullptr;
     stamp(sr, 0);
 
     // the prelude's global reads, issued together: every group window (raw
@@ -891,11 +891,10 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     stamp(sr, 4);  // end (chunk starts and each chunk's first root segment written)
 }
 
-}  // namespace
-
-// The merge phase over segment lists: one workgroup per row, lists in LDS when
-// they fit.
-hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
+// The merge phase over segment lists: the first stage over every group of
+// chunks, then the second stage (or, for very long rows, the row merge).
+template <bool ST>
+hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
     const bool wt = sh.weighted;
     const int ng = (sh.m + kGroup - 1) / kGroup;
     const unsigned R = (unsigned)sh.rows;
@@ -903,11 +902,11 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     timed_begin(kPhaseMerge, st);
     const dim3 grid(R * (unsigned)ng);
     if (ws.f64) {
-        if (wt) hipLaunchKernelGGL((k_group_merge<true, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        else hipLaunchKernelGGL((k_group_merge<false, double>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, double, false>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, double, false>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
     } else {
-        if (wt) hipLaunchKernelGGL((k_group_merge<true, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        else hipLaunchKernelGGL((k_group_merge<false, float>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, float, ST>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, float, ST>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
     }
     timed_end(st);
     if (two_stage_merge(sh.m)) {
@@ -917,16 +916,16 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
             static std::once_flag attr_once;
             std::call_once(attr_once, [] {
                 const int maxb = (int)top_lds_bytes(kTopMax, kTopMax * kGroup);
-                (void)hipFuncSetAttribute((const void*)k_top_merge<true>,
+                (void)hipFuncSetAttribute((const void*)k_top_merge<true, ST>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-                (void)hipFuncSetAttribute((const void*)k_top_merge<false>,
+                (void)hipFuncSetAttribute((const void*)k_top_merge<false, ST>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
             });
             timed_begin(kPhaseMergeTop, st);
             if (wt)
-                hipLaunchKernelGGL(k_top_merge<true>, dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+                hipLaunchKernelGGL((k_top_merge<true, ST>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
             else
-                hipLaunchKernelGGL(k_top_merge<false>, dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+                hipLaunchKernelGGL((k_top_merge<false, ST>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
             timed_end(st);
         }
         return hipGetLastError();
@@ -936,11 +935,19 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     *rec_done = true;
     timed_begin(kPhaseMergeTop, st);
     if (wt)
-        hipLaunchKernelGGL(k_merge_rows<true>, dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<true, ST>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     else
-        hipLaunchKernelGGL(k_merge_rows<false>, dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<false, ST>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     timed_end(st);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
+    // phase stamps (measurement only, f32 input) come from separate instances
+    if (ws.st_group != nullptr && !ws.f64) return launch_segment_merge_t<true>(sh, ws, st, rec_done);
+    return launch_segment_merge_t<false>(sh, ws, st, rec_done);
 }
 
 }  // namespace iso
