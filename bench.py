@@ -312,8 +312,12 @@ STAMP_PHASES = {
     "chunk_hulls": ((0, 1, "loads, sums, scan"), (1, 5, "first quickhull level"), (5, 2, "later levels"),
                     (2, 4, "slot and window writes"), (0, 4, "whole workgroup")),
     "group_merge": ((0, 1, "prelude (window reads, starts)"), (1, 2, "merge tree"),
+                    (1, 5, "tree level 0 (node 0)"), (5, 6, "tree level 1"), (6, 7, "tree level 2"),
+                    (7, 8, "tree level 3"), (8, 9, "tree level 4"), (9, 10, "tree level 5"),
                     (2, 3, "group list and window"), (3, 4, "descriptors out"), (0, 4, "whole workgroup")),
     "top_merge": ((0, 1, "prelude (group windows, starts)"), (1, 2, "merge tree"),
+                  (1, 5, "tree level 0 (node 0)"), (5, 6, "tree level 1"), (6, 7, "tree level 2"),
+                  (7, 8, "tree level 3"), (8, 9, "tree level 4"), (9, 10, "tree level 5"),
                   (2, 3, "root list and prefix"), (3, 4, "chunk starts, first segments"),
                   (0, 4, "whole workgroup")),
     "expand": ((0, 1, "record"), (1, 4, "stores"), (0, 4, "whole workgroup")),
@@ -341,7 +345,7 @@ def phase_stamps(b, y, calls=5):
         assert iso.iso_fit_ex(y.data_ptr(), None, R, N, out.data_ptr(), None, ws.data_ptr(), nb, b.sh,
                               flags | iso.ISO_F_NOCHECK) == 0
         b.stream.synchronize()
-        st = ws[nb0:nb0 + (2 * R * m + R * ng + R) * 64].view(torch.int64).cpu().numpy().reshape(-1, 8)
+        st = ws[nb0:nb0 + (2 * R * m + R * ng + R) * 128].view(torch.int64).cpu().numpy().reshape(-1, 16)
         parts = {"chunk_hulls": st[:R * m], "group_merge": st[R * m:R * m + R * ng],
                  "top_merge": st[R * m + R * ng:R * m + R * ng + R],
                  "expand": st[R * m + R * ng + R:]}

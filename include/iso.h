@@ -50,6 +50,9 @@
  *                        Nothing launched.
  *   ISO_ERR_DATA         iso_calib_fit got a non-finite score or outcome, or
  *                        (with segments) a negative score or segment id.
+ *   ISO_ERR_INVARIANT    (ISO_F_DEBUG_INVARIANTS) a segment list of the merge
+ *                        broke Definition 4.3 / Theorem 4.4 or the root
+ *                        chain was not convex.
  *   rows == 0 or n == 0 is a no-op that returns ISO_OK.
  *
  * The two warning/error statuses that depend on the data (NONFINITE, WEIGHT)
@@ -75,7 +78,8 @@ enum {
     ISO_ERR_NOMEM = -3,
     ISO_ERR_HIP = -4,
     ISO_ERR_WORKSPACE = -5,
-    ISO_ERR_DATA = -6
+    ISO_ERR_DATA = -6,
+    ISO_ERR_INVARIANT = -7
 };
 
 enum {
@@ -90,6 +94,20 @@ enum {
      * result; more memory traffic.  Needs the larger workspace that
      * iso_workspace_bytes reports for this flag. */
     ISO_F_COPY_CONTROL = 4u,
+    /* Tests: check the merge's segment lists on the device (paper section 4,
+     * Definition 4.3, Theorem 4.4): after every segment-list merge level, each
+     * list holds at most one segment per chunk of its range, in strictly
+     * increasing chunk order, with lo <= hi; each row's root list starts at
+     * the row's first point, ends at its last, keeps every segment inside its
+     * chunk hull, and its vertices form a convex chain (no right turn beyond
+     * rounding).  Also counts which merge paths ran.  The counters, 8 uint64,
+     * sit at the end of the workspace (pass the flag to iso_workspace_bytes),
+     * after any phase stamps: [0] violations, [1] chunk hulls rebuilt after
+     * the chunk kernel gave up, [2] thread walks handed to a wave, [3] nested
+     * bisections, [4] three-case searches, [5] levels checked, [6] root
+     * vertices checked.  A checked call returns ISO_ERR_INVARIANT when [0] is
+     * not zero.  Long rows only; slower. */
+    ISO_F_DEBUG_INVARIANTS = 8u,
     /* For iso_workspace_bytes only: size the workspace for a weighted call
      * (w != NULL).  Ignored by the fitting calls. */
     ISO_F_WEIGHTED_HINT = 0x100u,
@@ -98,13 +116,24 @@ enum {
      * device's 100 MHz real-time counter at its phase boundaries.  The stamps
      * take 64 bytes per workgroup at the end of the workspace (pass the flag to
      * iso_workspace_bytes too), from byte iso_workspace_bytes(rows, n, flags
-     * without this bit) on: rows*m rows of 8 uint64 for the chunk kernel, then
+     * without this bit) on: rows*m rows of 16 uint64 for the chunk kernel, then
      * rows*ng for the first merge stage (ng = ceil(m / 64)), rows for the
      * second stage, rows*m for the expansion (m = ceil(n / iso_chunk_size(n))).
      * Slots: chunk 0 start, 1 loads/sums/scan, 5 first quickhull level, 2 hull
      * built, 4 end; merge stages 0 start, 1 prelude, 2 merge tree, 3 lists and
-     * windows written, 4 end; expansion 0 start, 1 record ready, 4 end. */
-    ISO_F_PHASE_STAMPS = 0x200u
+     * windows written, 4 end, 5 + l node 0 through level l of a compact
+     * merge tree; expansion 0 start, 1 record ready, 4 end. */
+    ISO_F_PHASE_STAMPS = 0x200u,
+    /* Merge-schedule variants (measurement and stress; paper section 7.4 and
+     * appendix A).  Same result.  WAVE_MERGES: every merge of a segment-list
+     * level is run by a wave (default: a thread per merge when a level has more
+     * merges than the workgroup has waves, with walks that reach their cap
+     * handed to waves).  THREE_CASE: at the levels with a thread per merge,
+     * walks are capped at 8 (r + log2 C) steps (r the tree level, C the chunk
+     * size) and finished by the three-case bridge search of Lemma A.1.  The
+     * compact-array merges of short hulls are not affected. */
+    ISO_F_WAVE_MERGES = 0x400u,
+    ISO_F_THREE_CASE = 0x800u
 };
 
 /*

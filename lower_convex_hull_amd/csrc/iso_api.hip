@@ -30,11 +30,13 @@ struct Plan {
     size_t off_desc = 0, off_node_cnt = 0, off_vb = 0, off_rec = 0, off_desc_scr = 0, off_mi = 0;
     size_t off_gwin = 0, off_gtot = 0, off_cst = 0, off_gpre = 0, off_root_n = 0, off_ck_S = 0, off_ck_W = 0, off_rslope = 0;
     size_t off_stamps = 0;  // phase stamps (ISO_F_PHASE_STAMPS), at the end
+    size_t off_dbg = 0;     // debug counters (ISO_F_DEBUG_INVARIANTS), after the stamps
     size_t off_cp_a = 0, off_cp_b = 0, off_cp_off = 0, off_cp_cnt = 0, off_cp_off2 = 0,
            off_cp_cnt2 = 0, off_cp_cut = 0, off_cp_cut2 = 0;
 };
 
-bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p, bool stamps = false) {
+bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p, bool stamps = false,
+          bool debug = false) {
     *p = Plan();
     if (rows < 0 || n < 0) return false;
     if (rows == 0 || n == 0) return true;
@@ -97,6 +99,7 @@ bool plan(int64_t rows, int64_t n, bool weighted, bool copy_control, Plan* p, bo
         p->off_cp_cut2 = take(M * sizeof(int32_t));
     }
     if (stamps) p->off_stamps = take((2 * M + NG + R) * iso::kStampSlots * sizeof(uint64_t));
+    if (debug) p->off_dbg = take(iso::kDbgCount * sizeof(uint64_t));
     p->bytes = at;
     return true;
 }
@@ -116,6 +119,7 @@ iso::LongWs long_ws(void* base, const Plan& p, bool weighted, bool copy_control,
         ws.st_top = ws.st_group + NG * iso::kStampSlots;
         ws.st_expand = ws.st_top + rows * iso::kStampSlots;
     }
+    if (p.off_dbg) ws.dbg = at<unsigned long long>(base, p.off_dbg);
     ws.chunk_flag = at<int32_t>(base, p.off_chunk_flag);
     ws.tot_S = at<double>(base, p.off_tot_S);
     ws.tot_W = weighted ? at<double>(base, p.off_tot_W) : nullptr;
@@ -160,8 +164,9 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
     return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
-constexpr uint32_t kKnownFlags =
-    ISO_F_NOCHECK | ISO_F_DECREASING | ISO_F_COPY_CONTROL | ISO_F_WEIGHTED_HINT | ISO_F_PHASE_STAMPS;
+constexpr uint32_t kKnownFlags = ISO_F_NOCHECK | ISO_F_DECREASING | ISO_F_COPY_CONTROL |
+                                  ISO_F_DEBUG_INVARIANTS | ISO_F_WEIGHTED_HINT | ISO_F_PHASE_STAMPS |
+                                  ISO_F_WAVE_MERGES | ISO_F_THREE_CASE;
 
 // Launch timing (benchmarks only).
 struct Timing {
@@ -201,7 +206,9 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
     const bool weighted = w != nullptr;
     const bool copy_control = (flags & ISO_F_COPY_CONTROL) != 0;
     Plan p;
-    if (!plan(rows, n, weighted, copy_control, &p, (flags & ISO_F_PHASE_STAMPS) != 0)) return ISO_ERR_ARG;
+    if (!plan(rows, n, weighted, copy_control, &p, (flags & ISO_F_PHASE_STAMPS) != 0,
+              (flags & ISO_F_DEBUG_INVARIANTS) != 0))
+        return ISO_ERR_ARG;
     const size_t nb = (size_t)rows * (size_t)n * sizeof(T);
     const size_t ib = (size_t)rows * (size_t)n * sizeof(int32_t);
     if (overlaps(out, nb, y, nb) || overlaps(out, nb, w, nb) || overlaps(block_id, ib, y, nb) ||
@@ -221,6 +228,8 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
     } else {
         iso::LongShape sh{rows, n, p.m, weighted, sign};
         iso::LongWs ws = long_ws(workspace, p, weighted, copy_control, rows);
+        ws.sched = ((flags & ISO_F_WAVE_MERGES) ? iso::kSchedWaveAll : 0) |
+                   ((flags & ISO_F_THREE_CASE) ? iso::kSchedThreeCase : 0);
         e = iso::launch_long<T>(y, w, sh, ws, out, block_id, copy_control, st);
     }
     if (e != hipSuccess) return ISO_ERR_HIP;
@@ -231,7 +240,13 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
     int32_t any = 0;
     if (hipMemcpyAsync(&any, all, sizeof(any), hipMemcpyDeviceToHost, st) != hipSuccess)
         return ISO_ERR_HIP;
+    unsigned long long viol = 0;
+    if (p.long_rows && p.off_dbg &&
+        hipMemcpyAsync(&viol, at<unsigned long long>(workspace, p.off_dbg) + iso::kDbgViolations,
+                       sizeof(viol), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return ISO_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return ISO_ERR_HIP;
+    if (viol) return ISO_ERR_INVARIANT;
     if (any & iso::kFlagWeight) return ISO_ERR_WEIGHT;
     if (any & iso::kFlagNonfinite) return ISO_WARN_NONFINITE;
     return ISO_OK;
@@ -381,6 +396,7 @@ const char* iso_status_str(int status) {
         case ISO_ERR_HIP: return "HIP runtime error";
         case ISO_ERR_WORKSPACE: return "workspace too small";
         case ISO_ERR_DATA: return "non-finite score or outcome, or a negative score or segment";
+        case ISO_ERR_INVARIANT: return "a segment-list invariant of the merge was violated (debug check)";
         default: return "unknown status";
     }
 }
@@ -391,7 +407,7 @@ int64_t iso_short_row_max(void) { return iso::kShortMax; }
 size_t iso_workspace_bytes(int64_t rows, int64_t n, uint32_t flags) {
     Plan p;
     if (!plan(rows, n, (flags & ISO_F_WEIGHTED_HINT) != 0, (flags & ISO_F_COPY_CONTROL) != 0, &p,
-              (flags & ISO_F_PHASE_STAMPS) != 0))
+              (flags & ISO_F_PHASE_STAMPS) != 0, (flags & ISO_F_DEBUG_INVARIANTS) != 0))
         return 0;
     return p.bytes;
 }

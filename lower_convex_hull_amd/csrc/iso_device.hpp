@@ -373,6 +373,95 @@ __device__ __forceinline__ Bridge bisect_bridge(const V X, const List<DT> Lq, co
     return Bridge{A, B};
 }
 
+__device__ __forceinline__ bool same(Cur a, Cur b) { return a.seg == b.seg && a.pos == b.pos; }
+
+// Debug counter increment (no-op when the counters are off).
+__device__ __forceinline__ void dbg_add(unsigned long long* dbg, int k, unsigned long long v = 1) {
+    if (dbg && v) atomicAdd(dbg + k, v);
+}
+
+// The start of the middle edge of the list range [c0, c1] (c0 before c1):
+// within one segment, the middle vertex pair; across segments, the edge from
+// the middle segment's last vertex to the next segment's first (an edge of
+// the chain, as consecutive vertices of the hull).
+template <class DT>
+__device__ __forceinline__ Cur mid_edge(const List<DT> Lq, Cur c0, Cur c1) {
+    if (c0.seg == c1.seg) return Cur{c0.seg, (c0.pos + c1.pos - 1) >> 1};
+    const int sm = (c0.seg + c1.seg - 1) >> 1;
+    return Cur{sm, dhi(Lq.d[sm])};
+}
+
+// The three-case bridge search (paper appendix A, Lemma A.1, with lower
+// hulls): for the non-convex case (the shared point s is not a vertex of the
+// merged hull), keep a candidate range on each side ([a0, a1] of L without s,
+// [b0, b1] of R without s) and compare the middle edge alpha of L's range with
+// the middle edge beta of R's range, through the segment l r joining their
+// midpoints:
+//   (1) slope(alpha) >= slope(lr): the bridge's left end a* is not right of
+//       alpha's left end;
+//   (2) slope(lr) >= slope(beta): its right end b* is not left of beta's
+//       right end;
+//   (3) otherwise the lines of alpha and beta meet at gamma; if x(gamma) <=
+//       x(s), a* is not left of alpha's right end; if x(gamma) >= x(s), b* is
+//       not right of beta's left end.
+// Each case discards a prefix or suffix of one range.  When one range is a
+// single vertex, the bridge's other end is the tangent from it (a bisection
+// with a turn predicate).  Slopes are compared by cross multiplication (the
+// abscissa differences are positive); x(gamma) against x(s) by the sign of
+// the difference of the two lines at x(s), scaled by both abscissa spans.
+template <class V, class DT>
+__device__ __forceinline__ Bridge three_case_bridge(const V X, const List<DT> Lq, const List<DT> Rq, int jr,
+                                                    int* steps) {
+    const Cur sR = Rq.first();
+    const Pt S = Rq.pt(X, sR, jr);
+    auto rel = [&](Pt p) { return Pt{p.w - S.w, p.s - S.s}; };
+    Cur a0 = Lq.first(), a1 = Lq.prev(Lq.last());
+    Cur b0 = Rq.next(sR), b1 = Rq.last();
+    int it = 0;
+    for (; it < 4 * 64 * 16 && !same(a0, a1) && !same(b0, b1); ++it) {
+        const Cur am = mid_edge(Lq, a0, a1), an = Lq.next(am);
+        const Cur bm = mid_edge(Rq, b0, b1), bn = Rq.next(bm);
+        const Pt A0 = rel(Lq.pt(X, am, jr)), A1 = rel(Lq.pt(X, an, jr));
+        const Pt B0 = rel(Rq.pt(X, bm, jr)), B1 = rel(Rq.pt(X, bn, jr));
+        const double daw = A1.w - A0.w, das = A1.s - A0.s;
+        const double dbw = B1.w - B0.w, dbs = B1.s - B0.s;
+        const double lrw = (B0.w + B1.w) - (A0.w + A1.w), lrs = (B0.s + B1.s) - (A0.s + A1.s);
+        const bool c1 = __dmul_rn(das, lrw) >= __dmul_rn(lrs, daw);  // slope(alpha) >= slope(lr)
+        const bool c2 = __dmul_rn(lrs, dbw) >= __dmul_rn(dbs, lrw);  // slope(lr) >= slope(beta)
+        if (c1) a1 = am;
+        if (c2) b0 = bn;
+        if (!c1 && !c2) {
+            const double ca = __dmul_rn(A0.s, daw) - __dmul_rn(das, A0.w);
+            const double cb = __dmul_rn(B0.s, dbw) - __dmul_rn(dbs, B0.w);
+            const double D = __dmul_rn(ca, dbw) - __dmul_rn(cb, daw);
+            if (D <= 0.0) a0 = an;
+            if (D >= 0.0) b1 = bm;
+        }
+    }
+    *steps = it;
+    Bridge br;
+    if (same(a0, a1)) {
+        // a* is a0: b* is where the tangent from it touches R's range (the
+        // rightmost point of contact)
+        br.A = a0;
+        const Pt Pa = Lq.pt(X, a0, jr);
+        br.B = find_first(Rq, b0, b1, [&](Cur r) -> bool {
+            if (same(r, b1)) return true;
+            return cross3(Pa, Rq.pt(X, r, jr), Rq.pt(X, Rq.next(r), jr)) > 0.0;
+        });
+    } else {
+        // b* is b0: a* is where the tangent from it touches L's range (the
+        // leftmost point of contact)
+        br.B = b0;
+        const Pt Pb = Rq.pt(X, b0, jr);
+        br.A = find_first(Lq, a0, a1, [&](Cur l) -> bool {
+            if (same(l, a1)) return true;
+            return cross3(Lq.pt(X, l, jr), Lq.pt(X, Lq.next(l), jr), Pb) <= 0.0;
+        });
+    }
+    return br;
+}
+
 // For the 64 lanes of a wave: the vertex `lane` positions before (dir < 0) or
 // after (dir > 0) cursor C along the list, or valid = false past its end.
 // Every lane of the wave must call it with the same C and dir.
@@ -763,7 +852,8 @@ __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r
 // levels (u a multiple of 2, 4, 8) land on waves of different SIMDs (wave w
 // runs on SIMD w mod 4).
 template <int NT>
-__device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_t* ver, int nn, int E) {
+__device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_t* ver, int nn, int E,
+                                             uint64_t* sr = nullptr /* phase stamps */) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -789,6 +879,7 @@ __device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_
                     __hip_atomic_store(ver + a, lv + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 wave_sync();  // the wave's next merge reads the count
+                if (a == 0 && lv < 8) stamp(sr, 5 + lv);  // node 0 through level lv
             }
         }
     }

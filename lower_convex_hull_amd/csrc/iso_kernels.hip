@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kLongNT) void k_chunk_redo(const T* __restrict__ y,
     for (int64_t gid = blockIdx.x; gid < nchunks; gid += gridDim.x) {
         if (!(ws.chunk_flag[gid] & kChunkRedo)) continue;  // uniform: one load per workgroup
         chunk_hull<kLongNT, kLongP, kHullChains, WT, T>(y, w, n, m, sign, ws, full_slots, sm, gid);
+        if (threadIdx.x == 0) dbg_add(ws.dbg, kDbgRebuilt);
         __syncthreads();
     }
 }
@@ -406,7 +407,16 @@ __global__ __launch_bounds__(256) void k_copy_probe(const float4* __restrict__ s
     }
 }
 
+__global__ void k_zero_u64(unsigned long long* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
+}
+
 }  // namespace
+
+hipError_t launch_zero_u64(unsigned long long* p, int n, hipStream_t st) {
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, st, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t st) {
     const int64_t n16 = (int64_t)(bytes / 16);
@@ -445,6 +455,10 @@ hipError_t launch_long(const T* y, const T* w, const LongShape& sh, const LongWs
     ws.n = sh.n;
     ws.sign = sh.sign;
     ws.f64 = sizeof(T) == 8;
+    if (ws.dbg) {
+        const hipError_t e = launch_zero_u64(ws.dbg, kDbgCount, st);
+        if (e != hipSuccess) return e;
+    }
     // the copy control reads every chunk hull from its slot
     const int full_slots = copy_control ? 1 : 0;
     // phase stamps (measurement only) come from separate instances of the

@@ -32,8 +32,26 @@ constexpr int kWalkCap = 64;      // thread-walk steps before a merge is handed 
 constexpr int kWaveWalkCap = 64;  // wave-walk steps (63 vertices each) before bisection
 constexpr int kHardCap = 256;     // merges per level a wave may take over
 
+// Merge schedule variants (the paper's appendix A and section 7.4; measurement
+// and stress only): every merge of a segment-list level by a wave, instead of
+// a thread per merge with long walks handed to waves; or, at the levels run
+// with a thread per merge, walks capped at 8 (r + log2 C) steps followed by
+// the three-case bridge search instead of handing the merge to a wave.
+constexpr int kSchedWaveAll = 1;
+constexpr int kSchedThreeCase = 2;
+
+// Debug counters (ISO_F_DEBUG_INVARIANTS), 8 x uint64 at the end of the workspace.
+constexpr int kDbgViolations = 0;   // segment-list invariants found broken
+constexpr int kDbgRebuilt = 1;      // chunk hulls rebuilt after the chunk kernel gave up
+constexpr int kDbgToWave = 2;       // thread walks that reached their cap and went to a wave
+constexpr int kDbgBisect = 3;       // nested bisections (walks beyond every cap)
+constexpr int kDbgThreeCase = 4;    // three-case bridge searches
+constexpr int kDbgLevels = 5;       // segment-list merge levels checked
+constexpr int kDbgRootVerts = 6;    // root vertices checked for convexity
+constexpr int kDbgCount = 8;
+
 // Phase stamps per workgroup (ISO_F_PHASE_STAMPS).
-constexpr int kStampSlots = 8;
+constexpr int kStampSlots = 16;
 
 // Per-row data flags written by the kernels (read back by the checking path).
 constexpr int kFlagNonfinite = 1;
@@ -123,6 +141,10 @@ struct LongWs {
     int2* merge_info;     // [R*m] per merge: kept segments of L, first kept segment of R
     ChunkRec* rec;        // [R*m]
     int32_t* row_flag;    // [R]
+    // merge schedule variants (kSched* bits; 0 = the default schedule)
+    int sched;
+    // debug counters (null unless ISO_F_DEBUG_INVARIANTS), kDbg* indices
+    unsigned long long* dbg;
     // phase stamps (measurement only, null unless ISO_F_PHASE_STAMPS): per
     // workgroup kStampSlots 100 MHz real-time counter values
     uint64_t* st_chunk;   // [R*m]  chunk kernel
@@ -178,6 +200,9 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
 // The merge phase of the vertex-copying control (iso_copy.hip); leaves the
 // reconstruction records in ws.rec like the segment-list merge.
 hipError_t launch_copy_merge(const LongShape& sh, const LongWs& ws, hipStream_t st);
+
+// Clears the debug counters (a fill kernel, so that a captured graph may hold it).
+hipError_t launch_zero_u64(unsigned long long* p, int n, hipStream_t st);
 
 // Whether rows of m chunks take the two-stage merge (k_group_merge, then
 // k_top_merge when there is more than one group); longer rows take

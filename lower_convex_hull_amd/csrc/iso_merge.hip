@@ -13,6 +13,143 @@
 namespace iso {
 namespace {
 
+// ----------------------------------------------------------------------------
+// Two-stage merge.  Stage 1: one workgroup per group of kGroup consecutive
+// chunks merges their hulls (the tree's lower levels) with the chunk windows,
+// lists and starts in LDS.  Stage 2: one workgroup per row merges the group
+// hulls (the upper levels) with the group windows in LDS; a vertex outside a
+// group window is found through the group's segment list.  Every walk step
+// then reads LDS instead of a chain of cache misses.
+// ----------------------------------------------------------------------------
+
+// Schedule, debug counters and tree level of one segment-list merge level.
+struct MergeCtl {
+    int sched;                 // kSched* bits
+    unsigned long long* dbg;   // debug counters, or null
+    int r;                     // tree level: the merged nodes span 2^(r+1) chunks
+};
+
+// Runs one level of merges of the lists stored in D (slots a, a + span, ...):
+// a thread per merge when there are more merges than waves, handing walks that
+// run long to the waves; a wave per merge otherwise (or always, with
+// kSchedWaveAll).  With kSchedThreeCase the thread-per-merge walks are capped
+// at 8 (r + log2 C) steps and finished by the three-case search.  Then moves
+// each right list's kept descriptors down behind its left list's.  With debug
+// counters, checks every merged list: at most one segment per chunk (node) of
+// its range, in strictly increasing order, each with lo <= hi (Definition 4.3,
+// Theorem 4.4).
+template <int NT, bool EX, class V, class DT>
+__device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* CNT, int2* MI, int m, int span,
+                            int* s_nhard, int4* s_hard, int hard_cap, const MergeCtl ctl0) {
+    // the schedule variants and the debug checks exist only in the EX instances
+    const MergeCtl ctl = EX ? ctl0 : MergeCtl{0, nullptr, ctl0.r};
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
+    const int nm = (m - span + 2 * span - 1) / (2 * span);
+    if (nm > NW && !(ctl.sched & kSchedWaveAll)) {
+        if (tid == 0) *s_nhard = 0;
+        __syncthreads();
+        const bool three = EX && (ctl.sched & kSchedThreeCase) != 0;
+        const int cap = three ? 8 * (ctl.r + 12) : kWalkCap;  // log2 C = 12
+        for (int k = tid; k < nm; k += NT) {
+            const int a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br;
+            if (!bridge_start(X, Lq, Rq, b, br.A, br.B) && !walk_thread(X, Lq, Rq, b, br.A, br.B, cap)) {
+                if constexpr (EX) {
+                    if (three) {
+                        int st;
+                        br = three_case_bridge(X, Lq, Rq, b, &st);
+                        dbg_add(ctl.dbg, kDbgThreeCase);
+                        apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+                        continue;
+                    }
+                }
+                {
+                    int h = atomicAdd(s_nhard, 1);
+                    if (h < hard_cap) {
+                        s_hard[h] = make_int4(k, br.A.seg, br.A.pos, br.B.seg);
+                        MI[k] = make_int2(br.B.pos, 0);  // parked until the wave finishes it
+                        dbg_add(ctl.dbg, kDbgToWave);
+                        continue;
+                    }
+                    br = bisect_bridge(X, Lq, Rq, b);
+                    dbg_add(ctl.dbg, kDbgBisect);
+                }
+            }
+            apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+        __syncthreads();
+        const int nh = min(*s_nhard, hard_cap);
+        for (int h = wid; h < nh; h += NW) {
+            const int4 hk = s_hard[h];
+            const int k = hk.x, a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br{Cur{hk.y, hk.z}, Cur{hk.w, MI[k].x}};
+            if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0) {
+                br = bisect_bridge(X, Lq, Rq, b);
+                dbg_add(ctl.dbg, kDbgBisect);
+            }
+            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+    } else {
+        for (int k = wid; k < nm; k += NW) {
+            const int a = 2 * k * span, b = a + span;
+            List<DT> Lq{D + a, CNT[a]};
+            List<DT> Rq{D + b, CNT[b]};
+            Bridge br;
+            if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
+                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0) {
+                    br = bisect_bridge(X, Lq, Rq, b);
+                    dbg_add(ctl.dbg, kDbgBisect);
+                }
+            }
+            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
+        }
+    }
+    __syncthreads();
+    int ts = NT / nm;
+    ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
+    const int teams = NT / ts;
+    const int lane = tid & (ts - 1);
+    for (int k = tid / ts; k < nm; k += teams) {
+        const int b = (2 * k + 1) * span;
+        const int rs = MI[k].y;
+        const int nr = CNT[b] - rs;
+        for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
+    }
+    __syncthreads();
+    for (int k = tid / ts; k < nm; k += teams) {
+        const int a = 2 * k * span, b = a + span;
+        const int nl = MI[k].x;
+        const int nr = CNT[b] - MI[k].y;
+        for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
+    }
+    __syncthreads();
+    if (EX && ctl.dbg) {
+        // every node of the next level: a = 0, 2 span, ...
+        unsigned long long bad = 0;
+        for (int a = 2 * span * tid; a < m; a += 2 * span * NT) {
+            const int n = CNT[a], hi_node = min(m, a + 2 * span);
+            if (n < 1 || n > hi_node - a) {
+                ++bad;
+                continue;
+            }
+            int prev = a - 1;
+            for (int i = 0; i < n; ++i) {
+                const DT d = D[a + i];
+                const int c = dchunk(d);
+                if (c <= prev || c >= hi_node || dlo(d) > dhi(d) || dlo(d) < 0) ++bad;
+                prev = c;
+            }
+        }
+        dbg_add(ctl.dbg, kDbgViolations, bad);
+        if (tid == 0) dbg_add(ctl.dbg, kDbgLevels);
+    }
+}
+
 // Rows beyond the two-stage merge: after the first stage (k_group_merge, every
 // group of kGroup chunks merged in parallel, its list left at its first chunk's
 // slot), one workgroup per row runs the remaining levels of the merge tree with
@@ -20,8 +157,11 @@ namespace {
 // bridge and cuts the two boundary segments in place; then teams of threads
 // move each right list's remaining descriptors down behind the left list's
 // (through a scratch copy, since the two ranges may overlap).
-template <bool WT, bool ST>
+// MODE: 0 the production instance, 1 with phase stamps, 2 with the debug checks
+// and schedule variants.
+template <bool WT, int MODE>
 __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
+    constexpr bool ST = MODE == 1, EX = MODE == 2;
     constexpr int NT = kMergeNT;
     __shared__ double red[NT / 64 + 1];
     __shared__ int ired[NT / 64 + 1];
@@ -83,76 +223,10 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
               STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
 
-    // ---- the merge tree's remaining levels
-    for (int span = kGroup; span < m; span <<= 1) {
-        const int nm = (m - span + 2 * span - 1) / (2 * span);
-        if (nm > NW) {
-            // many merges: a thread each; walks that run long go to the waves
-            if (tid == 0) s_nhard = 0;
-            __syncthreads();
-            for (int k = tid; k < nm; k += NT) {
-                const int a = 2 * k * span, b = a + span;
-                List<uint2> Lq{D + a, CNT[a]};
-                List<uint2> Rq{D + b, CNT[b]};
-                Bridge br;
-                if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
-                    !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
-                    int h = atomicAdd(&s_nhard, 1);
-                    if (h < kHardCap) {
-                        s_hard[h] = make_int4(k, br.A.seg, br.A.pos, (br.B.seg << 16) | br.B.pos);
-                        continue;
-                    }
-                    br = bisect_bridge(X, Lq, Rq, b);
-                }
-                apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-            __syncthreads();
-            const int nh = min(s_nhard, kHardCap);
-            for (int h = wid; h < nh; h += NW) {
-                const int4 hk = s_hard[h];
-                const int k = hk.x, a = 2 * k * span, b = a + span;
-                List<uint2> Lq{D + a, CNT[a]};
-                List<uint2> Rq{D + b, CNT[b]};
-                Bridge br{Cur{hk.y, hk.z}, Cur{hk.w >> 16, hk.w & 0xffff}};
-                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                    br = bisect_bridge(X, Lq, Rq, b);
-                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-        } else {
-            // few merges: a wave each
-            for (int k = wid; k < nm; k += NW) {
-                const int a = 2 * k * span, b = a + span;
-                List<uint2> Lq{D + a, CNT[a]};
-                List<uint2> Rq{D + b, CNT[b]};
-                Bridge br;
-                if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
-                    if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                        br = bisect_bridge(X, Lq, Rq, b);
-                }
-                if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-            }
-        }
-        __syncthreads();
-        // move the right lists' tails: teams of ts threads per merge
-        int ts = NT / nm;
-        ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
-        const int teams = NT / ts;
-        const int lane = tid & (ts - 1);
-        for (int k = tid / ts; k < nm; k += teams) {
-            const int b = (2 * k + 1) * span;
-            const int rs = MI[k].y;
-            const int nr = CNT[b] - rs;
-            for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
-        }
-        __syncthreads();
-        for (int k = tid / ts; k < nm; k += teams) {
-            const int a = 2 * k * span, b = a + span;
-            const int nl = MI[k].x;
-            const int nr = CNT[b] - MI[k].y;
-            for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
-        }
-        __syncthreads();
-    }
+    // ---- the merge tree's remaining levels (tree level r: span 2^r chunks)
+    for (int span = kGroup, r = 6; span < m; span <<= 1, ++r)
+        merge_level<NT, EX>(X, D, SCR, CNT, MI, m, span, &s_nhard, s_hard, kHardCap,
+                            MergeCtl{ws.sched, ws.dbg, r});
 
     stamp(sr, 2);  // merge tree done
     // ---- reconstruction records (Corollary 4.5)
@@ -160,91 +234,6 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     stamp(sr, 4);  // end
 }
 
-
-// ----------------------------------------------------------------------------
-// Two-stage merge.  Stage 1: one workgroup per group of kGroup consecutive
-// chunks merges their hulls (the tree's lower levels) with the chunk windows,
-// lists and starts in LDS.  Stage 2: one workgroup per row merges the group
-// hulls (the upper levels) with the group windows in LDS; a vertex outside a
-// group window is found through the group's segment list.  Every walk step
-// then reads LDS instead of a chain of cache misses.
-// ----------------------------------------------------------------------------
-
-// Runs one level of merges of the lists stored in D (slots a, a + span, ...):
-// a thread per merge when there are more merges than waves, handing walks that
-// run long to the waves; a wave per merge otherwise.  Then moves each right
-// list's kept descriptors down behind its left list's.
-template <int NT, class V, class DT>
-__device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* CNT, int2* MI, int m, int span,
-                            int* s_nhard, int4* s_hard, int hard_cap) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
-    const int nm = (m - span + 2 * span - 1) / (2 * span);
-    if (nm > NW) {
-        if (tid == 0) *s_nhard = 0;
-        __syncthreads();
-        for (int k = tid; k < nm; k += NT) {
-            const int a = 2 * k * span, b = a + span;
-            List<DT> Lq{D + a, CNT[a]};
-            List<DT> Rq{D + b, CNT[b]};
-            Bridge br;
-            if (!bridge_start(X, Lq, Rq, b, br.A, br.B) &&
-                !walk_thread(X, Lq, Rq, b, br.A, br.B, kWalkCap)) {
-                int h = atomicAdd(s_nhard, 1);
-                if (h < hard_cap) {
-                    s_hard[h] = make_int4(k, br.A.seg, br.A.pos, br.B.seg);
-                    MI[k] = make_int2(br.B.pos, 0);  // parked until the wave finishes it
-                    continue;
-                }
-                br = bisect_bridge(X, Lq, Rq, b);
-            }
-            apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-        }
-        __syncthreads();
-        const int nh = min(*s_nhard, hard_cap);
-        for (int h = wid; h < nh; h += NW) {
-            const int4 hk = s_hard[h];
-            const int k = hk.x, a = 2 * k * span, b = a + span;
-            List<DT> Lq{D + a, CNT[a]};
-            List<DT> Rq{D + b, CNT[b]};
-            Bridge br{Cur{hk.y, hk.z}, Cur{hk.w, MI[k].x}};
-            if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                br = bisect_bridge(X, Lq, Rq, b);
-            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-        }
-    } else {
-        for (int k = wid; k < nm; k += NW) {
-            const int a = 2 * k * span, b = a + span;
-            List<DT> Lq{D + a, CNT[a]};
-            List<DT> Rq{D + b, CNT[b]};
-            Bridge br;
-            if (!bridge_start(X, Lq, Rq, b, br.A, br.B)) {
-                if (!walk_wave(X, Lq, Rq, b, br.A, br.B, kWaveWalkCap) && wlane == 0)
-                    br = bisect_bridge(X, Lq, Rq, b);
-            }
-            if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
-        }
-    }
-    __syncthreads();
-    int ts = NT / nm;
-    ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
-    const int teams = NT / ts;
-    const int lane = tid & (ts - 1);
-    for (int k = tid / ts; k < nm; k += teams) {
-        const int b = (2 * k + 1) * span;
-        const int rs = MI[k].y;
-        const int nr = CNT[b] - rs;
-        for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
-    }
-    __syncthreads();
-    for (int k = tid / ts; k < nm; k += teams) {
-        const int a = 2 * k * span, b = a + span;
-        const int nl = MI[k].x;
-        const int nr = CNT[b] - MI[k].y;
-        for (int i = lane; i < nr; i += ts) D[a + nl + i] = SCR[b + i];
-    }
-    __syncthreads();
-}
 
 // Vertices of group hulls for the second stage: position p of group g's hull,
 // relative to group gr's first point.
@@ -291,8 +280,9 @@ struct GroupView {
     }
 };
 
-template <bool WT, typename T, bool ST>
+template <bool WT, typename T, int MODE>
 __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs ws) {
+    constexpr bool ST = MODE == 1, EX = MODE == 2;
     constexpr int NT = kGroupNT, G = kGroup, E = 2 * kWinK, EG = 2 * kGWinK;
     static_assert(G == 64, "one wave numbers a group's segments");
     // the generic path's chunk windows, or the fast path's compact arrays, or
@@ -361,6 +351,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
                 chunk_hull<NT, kChunk / NT, kHullChains, WT, float>(static_cast<const float*>(ws.y),
                                                                     static_cast<const float*>(ws.w), ws.n, m,
                                                                     ws.sign, ws, 0, hs, rb + j0 + i);
+            if (tid == 0) dbg_add(ws.dbg, kDbgRebuilt);
             __syncthreads();
         }
         ok = true;
@@ -420,7 +411,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             sfirst[i] = -1;
         }
         __syncthreads();
-        merge_arrays<NT>(ar, CNT, VER, gc, E);
+        merge_arrays<NT>(ar, CNT, VER, gc, E, sr);
         stamp(sr, 2);  // merge tree done (compact arrays)
         hg = CNT[0];
         // the group's list: one segment per run of a chunk's vertices
@@ -483,7 +474,8 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             __syncthreads();
         } else {
             for (int span = 1; span < gc; span <<= 1)
-                merge_level<NT>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2);
+                merge_level<NT, EX>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2,
+                                    MergeCtl{ws.sched, ws.dbg, 31 - __clz(span)});
         }
         stamp(sr, 2);  // merge tree done (segment lists)
         nseg = CNT[0];
@@ -580,8 +572,9 @@ __host__ __device__ inline size_t top_lds_main(int ng) {
 __host__ __device__ inline int top_root_cap(int ng, int m) { return m < ng * 2 * kGWinK ? m : ng * 2 * kGWinK; }
 inline size_t top_lds_bytes(int ng, int m) { return top_lds_main(ng) + (size_t)top_root_cap(ng, m) * 4; }
 
-template <bool WT, bool ST>
+template <bool WT, int MODE>
 __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) {
+    constexpr bool ST = MODE == 1, EX = MODE == 2;
     constexpr int NT = kTopNT, G = kGroup, E = 2 * kGWinK;
     extern __shared__ int4 top_lds[];
     __shared__ double red[NT / 64 + 1];
@@ -700,7 +693,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             s_ver[g] = 0;
         }
         __syncthreads();
-        merge_arrays<NT>(ar, CNT, s_ver, ng, E);
+        merge_arrays<NT>(ar, CNT, s_ver, ng, E, sr);
         stamp(sr, 2);  // merge tree done (compact arrays)
         const int hr = CNT[0];
         // one root segment per run of a chunk's vertices; its chunk into rcbuf
@@ -770,7 +763,8 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             __syncthreads();
         } else {
             for (int span = 1; span < ng; span <<= 1)
-                merge_level<NT>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap);
+                merge_level<NT, EX>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap,
+                                    MergeCtl{ws.sched, ws.dbg, 6 + 31 - __clz(span)});
         }
         stamp(sr, 2);  // merge tree done (segment lists)
 
@@ -891,9 +885,87 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     stamp(sr, 4);  // end (chunk starts and each chunk's first root segment written)
 }
 
+// Debug check of each row's root list (ISO_F_DEBUG_INVARIANTS): at most one
+// segment per chunk, in strictly increasing chunk order, each within its
+// chunk hull (Definition 4.3, Theorem 4.4); the list starts at the row's
+// first point and ends at its last; and every root vertex turns left or runs
+// straight with its neighbours (the root list is a convex chain: its vertices
+// include the hull's and lie on it).  Workgroup (row, part): part 0 checks the
+// list, every part a stride of the vertices.
+constexpr int kDbgParts = 64;
+template <bool WT>
+__global__ __launch_bounds__(256) void k_debug_root(int m, LongWs ws, int two_stage) {
+    const int64_t row = blockIdx.x / kDbgParts;
+    const int part = (int)(blockIdx.x - row * kDbgParts);
+    const int64_t rb = row * m;
+    const int tid = threadIdx.x;
+    if (ws.row_flag[row] & kFlagNonfinite) return;
+    const uint2* D = two_stage ? ws.desc_scr + rb : ws.desc + rb;
+    const int nroot = two_stage ? (ws.root_n[row] & ~kRootSlopes) : ws.node_cnt[rb];
+    const int32_t* HC = ws.hull_cnt + rb;
+    unsigned long long bad = 0;
+    if (nroot < 1 || nroot > m) {
+        if (part == 0 && tid == 0) dbg_add(ws.dbg, kDbgViolations);
+        return;
+    }
+    // a segment is readable when its chunk and positions lie within the chunk's hull
+    auto ok_seg = [&](uint2 d) {
+        const int c = dchunk(d);
+        return c >= 0 && c < m && dlo(d) <= dhi(d) && dhi(d) < HC[c] && HC[c] <= kChunk + 1;
+    };
+    if (part == 0) {
+        for (int i = tid; i < nroot; i += 256) {
+            const uint2 d = D[i];
+            if (!ok_seg(d)) ++bad;
+            if (i > 0 && dchunk(D[i - 1]) >= dchunk(d)) ++bad;
+        }
+        if (tid == 0) {
+            const uint2 f = D[0], l = D[nroot - 1];
+            if (dchunk(f) != 0 || dlo(f) != 0 || dchunk(l) != m - 1 || dhi(l) != HC[m - 1] - 1) ++bad;
+        }
+    }
+    // vertex v of the root chain: segment by binary search over the vertex prefix
+    const int32_t* vb = ws.vb + rb;
+    const uint2 dl = D[nroot - 1];
+    const int64_t nv64 = ok_seg(dl) ? (int64_t)vb[nroot - 1] + dhi(dl) - dlo(dl) + 1 : 0;
+    const int nv = (int)min(max(nv64, (int64_t)0), (int64_t)m * (kChunk + 1));
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
+                    ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT, inc_src(ws, row, m, 0)};
+    // vertex v, or false when the list does not hold it readably
+    auto vert = [&](int v, Pt& p) {
+        int lo = 0, hi = nroot - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (vb[mid] <= v) lo = mid;
+            else hi = mid - 1;
+        }
+        const uint2 d = D[lo];
+        const int pos = dlo(d) + (v - vb[lo]);
+        if (!ok_seg(d) || pos < dlo(d) || pos > dhi(d)) return false;
+        p = X.vtx(dchunk(d), pos, 0);
+        return true;
+    };
+    unsigned long long checked = 0;
+    for (int v = 1 + part * 256 + tid; v + 1 < nv; v += 256 * kDbgParts) {
+        Pt a, b, c;
+        if (!vert(v - 1, a) || !vert(v, b) || !vert(v + 1, c)) {
+            ++bad;
+            continue;
+        }
+        const double t1 = __dmul_rn(b.w - a.w, c.s - a.s), t2 = __dmul_rn(b.s - a.s, c.w - a.w);
+        // a right turn beyond rounding: the chain is not convex there
+        if (t1 - t2 < -1e-9 * (fabs(t1) + fabs(t2))) ++bad;
+        if (!(b.w > a.w)) ++bad;
+        ++checked;
+    }
+    dbg_add(ws.dbg, kDbgViolations, bad);
+    dbg_add(ws.dbg, kDbgRootVerts, checked);
+}
+
 // The merge phase over segment lists: the first stage over every group of
 // chunks, then the second stage (or, for very long rows, the row merge).
-template <bool ST>
+template <int MODE>
 hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
     const bool wt = sh.weighted;
     const int ng = (sh.m + kGroup - 1) / kGroup;
@@ -902,11 +974,11 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
     timed_begin(kPhaseMerge, st);
     const dim3 grid(R * (unsigned)ng);
     if (ws.f64) {
-        if (wt) hipLaunchKernelGGL((k_group_merge<true, double, false>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        else hipLaunchKernelGGL((k_group_merge<false, double, false>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, double, MODE == 1 ? 0 : MODE>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, double, MODE == 1 ? 0 : MODE>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
     } else {
-        if (wt) hipLaunchKernelGGL((k_group_merge<true, float, ST>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
-        else hipLaunchKernelGGL((k_group_merge<false, float, ST>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        if (wt) hipLaunchKernelGGL((k_group_merge<true, float, MODE>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
+        else hipLaunchKernelGGL((k_group_merge<false, float, MODE>), grid, dim3(kGroupNT), 0, st, sh.m, ng, ws);
     }
     timed_end(st);
     if (two_stage_merge(sh.m)) {
@@ -916,16 +988,16 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
             static std::once_flag attr_once;
             std::call_once(attr_once, [] {
                 const int maxb = (int)top_lds_bytes(kTopMax, kTopMax * kGroup);
-                (void)hipFuncSetAttribute((const void*)k_top_merge<true, ST>,
+                (void)hipFuncSetAttribute((const void*)k_top_merge<true, MODE>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-                (void)hipFuncSetAttribute((const void*)k_top_merge<false, ST>,
+                (void)hipFuncSetAttribute((const void*)k_top_merge<false, MODE>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
             });
             timed_begin(kPhaseMergeTop, st);
             if (wt)
-                hipLaunchKernelGGL((k_top_merge<true, ST>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+                hipLaunchKernelGGL((k_top_merge<true, MODE>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
             else
-                hipLaunchKernelGGL((k_top_merge<false, ST>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
+                hipLaunchKernelGGL((k_top_merge<false, MODE>), dim3(R), dim3(kTopNT), lds, st, sh.m, ng, ws);
             timed_end(st);
         }
         return hipGetLastError();
@@ -935,9 +1007,9 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
     *rec_done = true;
     timed_begin(kPhaseMergeTop, st);
     if (wt)
-        hipLaunchKernelGGL((k_merge_rows<true, ST>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<true, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     else
-        hipLaunchKernelGGL((k_merge_rows<false, ST>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<false, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
     timed_end(st);
     return hipGetLastError();
 }
@@ -946,8 +1018,18 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
 
 hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream_t st, bool* rec_done) {
     // phase stamps (measurement only, f32 input) come from separate instances
-    if (ws.st_group != nullptr && !ws.f64) return launch_segment_merge_t<true>(sh, ws, st, rec_done);
-    return launch_segment_merge_t<false>(sh, ws, st, rec_done);
+    // the debug checks and schedule variants, or else phase stamps (f32 input),
+    // come from separate instances of the merge kernels
+    hipError_t e;
+    if (ws.dbg || ws.sched) e = launch_segment_merge_t<2>(sh, ws, st, rec_done);
+    else if (ws.st_group != nullptr && !ws.f64) e = launch_segment_merge_t<1>(sh, ws, st, rec_done);
+    else e = launch_segment_merge_t<0>(sh, ws, st, rec_done);
+    if (e != hipSuccess || !ws.dbg) return e;
+    const dim3 grid((unsigned)(sh.rows * kDbgParts));
+    const int two = two_stage_merge(sh.m) ? 1 : 0;
+    if (sh.weighted) hipLaunchKernelGGL(k_debug_root<true>, grid, dim3(256), 0, st, sh.m, ws, two);
+    else hipLaunchKernelGGL(k_debug_root<false>, grid, dim3(256), 0, st, sh.m, ws, two);
+    return hipGetLastError();
 }
 
 }  // namespace iso

@@ -24,10 +24,14 @@ ISO_ERR_NOMEM = -3
 ISO_ERR_HIP = -4
 ISO_ERR_WORKSPACE = -5
 ISO_ERR_DATA = -6
+ISO_ERR_INVARIANT = -7
 
 ISO_F_NOCHECK = 1
 ISO_F_DECREASING = 2
 ISO_F_COPY_CONTROL = 4
+ISO_F_DEBUG_INVARIANTS = 8
+ISO_F_WAVE_MERGES = 0x400
+ISO_F_THREE_CASE = 0x800
 ISO_F_WEIGHTED_HINT = 0x100
 ISO_F_PHASE_STAMPS = 0x200
 

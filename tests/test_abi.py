@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in (0, 1, -1, -2, -3, -4, -5, -6):
+    for s in (0, 1, -1, -2, -3, -4, -5, -6, -7):
         assert iso.iso_status_str(s) and iso.iso_status_str(s) != "unknown status"
     assert iso.iso_status_str(42) == "unknown status"
 
