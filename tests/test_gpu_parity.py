@@ -438,6 +438,27 @@ def test_iso_fit_blocking_entry(torch):
     iso.iso_release()
 
 
+def test_iso_fit_reports_allocation_failure(torch):
+    """A shape whose workspace (about 1e13 bytes) is more than the device holds:
+    iso_fit's allocation fails, it returns ISO_ERR_NOMEM with nothing launched
+    (the tiny buffers passed are never read), and the library keeps working."""
+    n = 1 << 40
+    assert iso.iso_workspace_bytes(1, n, 0) > 10 ** 12
+    y = torch.zeros(16, dtype=torch.float32, device="cuda")
+    out = torch.full((16,), 7.0, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    assert iso.iso_fit(y.data_ptr(), None, 1, n, out.data_ptr()) == iso.ISO_ERR_NOMEM
+    torch.cuda.synchronize()
+    assert float(out.sum()) == 16 * 7.0
+    y2, _ = inputs.noisy(2, 20_000, 19)
+    yt = torch.from_numpy(y2).cuda()
+    o2 = torch.empty_like(yt)
+    assert iso.iso_fit(yt.data_ptr(), None, 2, 20_000, o2.data_ptr()) == iso.ISO_OK
+    _, z64, _ = oracle.fit_rows_f32(y2)
+    assert fitcheck.parity(y2, None, o2.cpu().numpy(), z64)[0]
+    iso.iso_release()
+
+
 def test_fit_wrapper_on_torch_stream(torch):
     y, _ = inputs.noisy(8, 7000, 17)
     yt = torch.from_numpy(y).cuda()
