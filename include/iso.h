@@ -43,6 +43,8 @@
  *   ISO_ERR_WEIGHT       some w_i <= 0 or non-finite (the problem needs
  *                        w_i > 0, section 2.1).  out is unspecified.
  *   ISO_ERR_NOMEM        iso_fit could not allocate its cached workspace.
+ *                        Nothing launched; the HIP runtime's last-error
+ *                        state that the failed hipMalloc set is cleared.
  *   ISO_ERR_HIP          a HIP runtime call or kernel launch failed.
  *   ISO_ERR_WORKSPACE    iso_fit_ex got a workspace smaller than
  *                        iso_workspace_bytes() asks for, or the shape needs

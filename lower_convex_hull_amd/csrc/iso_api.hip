@@ -306,7 +306,12 @@ int cached_fit(const T* y, const T* w, int64_t rows, int64_t n, T* out) {
         c.ptr[dev] = nullptr;
         c.bytes[dev] = 0;
         void* q = nullptr;
-        if (hipMalloc(&q, p.bytes) != hipSuccess) return ISO_ERR_NOMEM;
+        if (hipMalloc(&q, p.bytes) != hipSuccess) {
+            // A failed hipMalloc also sets the thread's last-error state; clear it so the
+            // caller's next launch check does not report this failure a second time.
+            (void)hipGetLastError();
+            return ISO_ERR_NOMEM;
+        }
         c.ptr[dev] = q;
         c.bytes[dev] = p.bytes;
     }

@@ -788,19 +788,20 @@ __device__ __forceinline__ void team_move(const Arr& ar, int l0, int A, int r0, 
 // lane), and walks only when neither finds exactly one pair.  Every lane of
 // the wave calls it.
 __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r0, int cR, int lane) {
+    // the loads of the shared-point test and of the 8 x 8 test are issued
+    // together (addresses clamped into the arrays), so that the common cases
+    // cost one round trip to LDS
+    const int a8 = cL - 2 - (lane & 7), b8 = 1 + (lane >> 3);
+    const int ac = max(a8, 0), bc = min(b8, cR - 1);
+    const Pt PA = ar.pt(l0 + cL - 2), Ps = ar.pt(r0), PB = ar.pt(r0 + 1);
+    const Pt La = ar.pt(l0 + ac), Ln = ar.pt(l0 + ac + 1), Rb = ar.pt(r0 + bc), Rp = ar.pt(r0 + bc - 1);
+    const Pt Lp = ar.pt(l0 + max(ac - 1, 0)), Rn = ar.pt(r0 + min(bc + 1, cR - 1));
+    if (cross3(PA, Ps, PB) > 0.0) return make_int2(cL - 1, 1);  // convex at the shared point
     {
-        const Pt PA = ar.pt(l0 + cL - 2), Ps = ar.pt(r0), PB = ar.pt(r0 + 1);
-        if (cross3(PA, Ps, PB) > 0.0) return make_int2(cL - 1, 1);  // convex at the shared point
-    }
-    {
-        // first the 8 x 8 pairs nearest the shared point, one per lane
-        const int a = cL - 2 - (lane & 7), b = 1 + (lane >> 3);
+        // the 8 x 8 pairs nearest the shared point, one per lane
         bool hit = false;
-        if (a >= 0 && b <= cR - 1) {
-            const Pt La = ar.pt(l0 + a), Ln = ar.pt(l0 + a + 1), Rb = ar.pt(r0 + b), Rp = ar.pt(r0 + b - 1);
-            const Pt Lp = a > 0 ? ar.pt(l0 + a - 1) : La;
-            const Pt Rn = b < cR - 1 ? ar.pt(r0 + b + 1) : Rb;
-            hit = (a == 0 || cross3(Lp, La, Rb) > 0.0) && (b == cR - 1 || cross3(La, Rb, Rn) > 0.0) &&
+        if (a8 >= 0 && b8 <= cR - 1) {
+            hit = (a8 == 0 || cross3(Lp, La, Rb) > 0.0) && (b8 == cR - 1 || cross3(La, Rb, Rn) > 0.0) &&
                   cross3(La, Ln, Rb) <= 0.0 && cross3(La, Rp, Rb) <= 0.0;
         }
         const uint64_t bal = __ballot(hit);
@@ -846,8 +847,9 @@ __device__ __forceinline__ int2 wave_bridge(const Arr& ar, int l0, int cL, int r
 // at every level belong to one wave, which records in ver[a] (LDS, zeroed by
 // the caller before its last barrier) how many levels node a has been
 // through; a merge waits only until its right node has been through every
-// level at which that node had a partner.  A wait is only ever for a lower
-// level, so every wait ends.  Nodes 4u .. 4u+3 belong to wave u mod NW, and
+// level at which that node had a partner (ver[a] also carries node a's vertex
+// count, so the waiting wave reads both at once).  A wait is only ever for a
+// lower level, so every wait ends.  Nodes 4u .. 4u+3 belong to wave u mod NW, and
 // with 16 waves u's two bit pairs swap, so that the few merges of the upper
 // levels (u a multiple of 2, 4, 8) land on waves of different SIMDs (wave w
 // runs on SIMD w mod 4).
@@ -869,14 +871,21 @@ __device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_
                 int need = 0;
                 for (int l2 = 0, s2 = 1; l2 < lv; ++l2, s2 <<= 1)
                     if (b + s2 < nn) need = l2 + 1;
-                while (__hip_atomic_load(ver + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need)
+                // ver[b] holds (levels done << 16) | b's vertex count since its
+                // first merge; before that b's count is its initial cnt[b]
+                const int cL = cnt[a], c0 = cnt[b];
+                int v;
+                while (((v = __hip_atomic_load(ver + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 16) <
+                       need)
                     __builtin_amdgcn_s_sleep(1);
-                const int cL = cnt[a], cR = cnt[b];
+                const int cR = need ? (v & 0xffff) : c0;
                 const int2 br = wave_bridge(ar, a * E, cL, b * E, cR, lane);
                 team_move(ar, a * E, br.x, b * E, br.y, cR, lane, 64, true);
                 if (lane == 0) {
-                    cnt[a] = br.x + 1 + cR - br.y;
-                    __hip_atomic_store(ver + a, lv + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    const int ca = br.x + 1 + cR - br.y;
+                    cnt[a] = ca;
+                    __hip_atomic_store(ver + a, ((lv + 1) << 16) | ca, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 wave_sync();  // the wave's next merge reads the count
                 if (a == 0 && lv < 8) stamp(sr, 5 + lv);  // node 0 through level lv
