@@ -341,65 +341,74 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
         // thread); the keys of a level in buffer lv & 1
         int ci = 0, kB = len, nv = 2, cb = 0, state = 0;
         Pt A{0.0, 0.0}, B{sm.end_w, sm.end_s};
+        // level 0 has one chord, from point 0 to point len: the thread's own
+        // points, from registers, without branches (with A at the origin the
+        // depth is cross3(A, P, B) term for term).  It runs before the level
+        // loop so that the register copies of the points end here.
+        unsigned long long qbest0 = 0ull;
+        if (alive) {
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                const int k = base + b + 1;
+                const double c = __dmul_rn(WT ? pw[b] : (double)k, B.s) - __dmul_rn(ps[b], B.w);
+                const bool live = ((alive >> b) & 1u) && c > 0.0;
+                if (!live) alive &= ~(1u << b);
+                const unsigned long long key = live ? mkkey(c, k) : 0ull;
+                qbest0 = key > qbest0 ? key : qbest0;
+            }
+        }
         __syncthreads();
         for (int lv = 0; lv < kQhLevels; ++lv) {
             unsigned long long* qkey = sm.qkey[lv & 1];
             const int32_t* vk = sm.qk[cb];
-            int qi = ci;                      // this thread's last chord
-            unsigned long long qbest = 0ull;  // and its best key there
-            if (alive) {
+            int qi = ci;                        // this thread's last chord
+            unsigned long long qbest = qbest0;  // and its best key there
+            qbest0 = 0ull;
+            if (lv > 0 && alive) {
+                // chord i runs from A to B (index nk); the next chords come
+                // from the list when this thread's points pass a vertex (a
+                // point that became a vertex lies on its chords and drops
+                // out).  The chord's differences are formed once per chord,
+                // and the next live point's coordinates are read while the
+                // current one is tested.
                 double bc = 0.0;
                 int bk = 0;
-                if (lv == 0) {
-                    // one chord, from point 0 to point len: the thread's own
-                    // points, from registers, without branches (with A at
-                    // the origin the depth is cross3(A, P, B) term for term)
-                    unsigned long long best = 0ull;
-#pragma unroll
-                    for (int b = 0; b < P; ++b) {
-                        const int k = base + b + 1;
-                        const double c = __dmul_rn(WT ? pw[b] : (double)k, B.s) - __dmul_rn(ps[b], B.w);
-                        const bool live = ((alive >> b) & 1u) && c > 0.0;
-                        if (!live) alive &= ~(1u << b);
-                        const unsigned long long key = live ? mkkey(c, k) : 0ull;
-                        best = key > best ? key : best;
+                int i = ci, nk = kB;
+                double Aw = A.w, As = A.s, dW = B.w - A.w, dS = B.s - A.s;
+                uint32_t mm = alive;
+                int b = lsb32(mm);
+                double Sn = pS[sk(base + b + 1)];
+                double Wn = WT ? pW[sk(base + b + 1)] : 0.0;
+                for (;;) {
+                    const int k = base + b + 1;
+                    const double Sk = Sn, Wk = WT ? Wn : (double)k;
+                    mm &= mm - 1u;
+                    const int b2 = mm ? lsb32(mm) : b;
+                    Sn = pS[sk(base + b2 + 1)];
+                    if (WT) Wn = pW[sk(base + b2 + 1)];
+                    if (k >= nk) {
+                        if (bk) atomicMax(&qkey[i], mkkey(bc, bk));
+                        bc = 0.0;
+                        bk = 0;
+                        do {
+                            ++i;
+                            nk = vk[i + 1];
+                        } while (nk <= k);
+                        Aw = sm.qW[cb][i];
+                        As = sm.qS[cb][i];
+                        dW = sm.qW[cb][i + 1] - Aw;
+                        dS = sm.qS[cb][i + 1] - As;
                     }
-                    qbest = best;
-                } else {
-                    // chord i runs from A to B (index nk); the next chords come
-                    // from the list when this thread's points pass a vertex
-                    // (a point that became a vertex lies on its chords and
-                    // drops out)
-                    int i = ci, nk = kB;
-                    Pt Ac = A, Bc = B;
-                    for (uint32_t mm = alive; mm; mm &= mm - 1u) {
-                        const int b = lsb32(mm);
-                        const int k = base + b + 1;
-                        if (k >= nk) {
-                            if (bk) atomicMax(&qkey[i], mkkey(bc, bk));
-                            bc = 0.0;
-                            bk = 0;
-                            do {
-                                ++i;
-                                nk = vk[i + 1];
-                            } while (nk <= k);
-                            Ac = Pt{sm.qW[cb][i], sm.qS[cb][i]};
-                            Bc = Pt{sm.qW[cb][i + 1], sm.qS[cb][i + 1]};
-                        }
-                        const Pt Pk{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
-                        const double c = cross3(Ac, Pk, Bc);
-                        if (c > 0.0) {
-                            if (c > bc) {
-                                bc = c;
-                                bk = k;
-                            }
-                        } else {
-                            alive &= ~(1u << b);
-                        }
-                    }
-                    qi = i;
-                    qbest = bk ? mkkey(bc, bk) : 0ull;
+                    const double c = __dmul_rn(Wk - Aw, dS) - __dmul_rn(Sk - As, dW);
+                    const bool better = c > bc;  // bc >= 0, so a better point is live
+                    alive = c > 0.0 ? alive : (alive & ~(1u << b));
+                    bc = better ? c : bc;
+                    bk = better ? k : bk;
+                    if (!mm) break;
+                    b = b2;
                 }
+                qi = i;
+                qbest = bk ? mkkey(bc, bk) : 0ull;
             }
             if (qbest) atomicMax(&qkey[qi], qbest);
             __syncthreads();
