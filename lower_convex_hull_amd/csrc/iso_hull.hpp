@@ -45,12 +45,15 @@ struct HullSmem {
     int ired[NT / 64 + 1];
     double end_s, end_w;          // S and W of point len (padding points repeat it)
     int flag;
-    // quickhull: every point's S (and W) at k + (k-1)/P (the region arrays
-    // serve where they exist), the vertex list (two buffers), and per chord
-    // the key of the farthest point below it
-    static constexpr int NP = MODE == kHullQuick ? NT * RS : 1;
-    double pS[NP];
-    double pW[WT ? NP : 1];
+    // quickhull: the points still live after the first level, compacted per
+    // wave in point order (S, W when weighted, and the block index; CW entries
+    // per wave; the region arrays serve where they exist), the vertex list
+    // (two buffers), and per chord the key of the farthest point below it
+    static constexpr int CW = MODE == kHullQuick ? kQhWaveCap : 64 * RS;
+    static constexpr int NC = MODE == kHullQuick ? (NT / 64) * kQhWaveCap : 1;
+    double cS[NC];
+    double cW[WT ? NC : 1];
+    uint16_t ck[NC];
     int32_t qk[2][NQ];
     double qS[2][NQ], qW[2][NQ];
     unsigned long long qkey[2][NQ];
@@ -296,21 +299,18 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
     // a few levels with few vertices; a block that needs more levels or more
     // vertices falls back to the chains and merges below.
     if constexpr (MODE != kHullChains) {
-        double* pS = MODE == kHullQuick ? sm.pS : sm.S;
-        double* pW = MODE == kHullQuick ? sm.pW : sm.W;
-        auto sk = [](int k) { return k + (k - 1) / P; };  // k >= 1
+        constexpr int CW = HullSmem<NT, P, WT, MODE>::CW;
+        double* cS = MODE == kHullQuick ? sm.cS : sm.S;
+        double* cW = MODE == kHullQuick ? sm.cW : sm.W;
+        uint16_t* cK = MODE == kHullQuick ? sm.ck : sm.idx;
         // the key of a candidate: the positive f64 depth measure with its low
-        // 13 bits giving way to the index, so that the largest key is the
+        // 13 bits giving way to the candidate's compact position (the thread's
+        // point number in the first level), so that the largest key is the
         // farthest point and, on a tie, the lowest index
-        auto mkkey = [](double c, int k) {
+        auto mkkey = [](double c, int e) {
             return ((unsigned long long)__double_as_longlong(c) & ~0x1fffull) |
-                   (unsigned long long)(0x1fff - k);
+                   (unsigned long long)(0x1fff - e);
         };
-#pragma unroll
-        for (int b = 0; b < P; ++b) {
-            pS[sk(base + b + 1)] = ps[b];
-            if (WT) pW[sk(base + b + 1)] = pw[b];
-        }
         // live points: candidates below point len
         uint32_t alive = 0;
         if (full) {
@@ -320,6 +320,14 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
 #pragma unroll
             for (int b = 0; b < P; ++b)
                 if (((cand >> (b + 1)) & 1u) && base + b + 1 < len) alive |= 1u << b;
+        }
+        {
+            // the thread's last point (base + P) is a candidate for the
+            // chains as their shared end; here it is tested like the others,
+            // against the next thread's first element (the wave's last lane
+            // keeps it)
+            const T nxt = __shfl_down(yv[0], 1);
+            if ((L & 63) != 63 && base + P < len && !(yv[P - 1] < nxt)) alive &= ~(1u << (P - 1));
         }
         if (L == 0) {
             sm.qk[0][0] = 0;
@@ -353,8 +361,41 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 const double c = __dmul_rn(WT ? pw[b] : (double)k, B.s) - __dmul_rn(ps[b], B.w);
                 const bool live = ((alive >> b) & 1u) && c > 0.0;
                 if (!live) alive &= ~(1u << b);
-                const unsigned long long key = live ? mkkey(c, k) : 0ull;
+                const unsigned long long key = live ? mkkey(c, b) : 0ull;
                 qbest0 = key > qbest0 ? key : qbest0;
+            }
+        }
+        // the points still live go to the wave's part of the compact arrays,
+        // in point order; this thread's start e0 there comes from a scan of
+        // the live counts over the wave.  A wave with more than CW live points
+        // stores nothing and the block falls back.
+        const uint32_t alive0 = alive;
+        int e0, over;
+        {
+            const int lane = L & 63;
+            const int cnt = __popc(alive);
+            int inc = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(inc, d);
+                if (lane >= d) inc += t;
+            }
+            e0 = (L >> 6) * CW + inc - cnt;
+            over = __shfl(inc, 63) > CW;
+            if (!over && alive) {
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    if ((alive >> b) & 1u) {
+                        const int e = e0 + __popc(alive & ((1u << b) - 1u));
+                        cS[e] = ps[b];
+                        if (WT) cW[e] = pw[b];
+                        cK[e] = (uint16_t)(base + b + 1);
+                    }
+                }
+            }
+            if (qbest0) {
+                const int b = (int)(0x1fff - (qbest0 & 0x1fffull));
+                qbest0 = (qbest0 & ~0x1fffull) | (unsigned long long)(0x1fff - (e0 + __popc(alive & ((1u << b) - 1u))));
             }
         }
         __syncthreads();
@@ -372,24 +413,26 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 // and the next live point's coordinates are read while the
                 // current one is tested.
                 double bc = 0.0;
-                int bk = 0;
+                int be = 0;
                 int i = ci, nk = kB;
                 double Aw = A.w, As = A.s, dW = B.w - A.w, dS = B.s - A.s;
                 uint32_t mm = alive;
                 int b = lsb32(mm);
-                double Sn = pS[sk(base + b + 1)];
-                double Wn = WT ? pW[sk(base + b + 1)] : 0.0;
+                int en = e0 + __popc(alive0 & ((1u << b) - 1u));
+                double Sn = cS[en];
+                double Wn = WT ? cW[en] : 0.0;
                 for (;;) {
-                    const int k = base + b + 1;
+                    const int k = base + b + 1, e = en;
                     const double Sk = Sn, Wk = WT ? Wn : (double)k;
                     mm &= mm - 1u;
                     const int b2 = mm ? lsb32(mm) : b;
-                    Sn = pS[sk(base + b2 + 1)];
-                    if (WT) Wn = pW[sk(base + b2 + 1)];
+                    en = e0 + __popc(alive0 & ((1u << b2) - 1u));
+                    Sn = cS[en];
+                    if (WT) Wn = cW[en];
                     if (k >= nk) {
-                        if (bk) atomicMax(&qkey[i], mkkey(bc, bk));
+                        if (bc > 0.0) atomicMax(&qkey[i], mkkey(bc, be));
                         bc = 0.0;
-                        bk = 0;
+                        be = 0;
                         do {
                             ++i;
                             nk = vk[i + 1];
@@ -403,15 +446,18 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                     const bool better = c > bc;  // bc >= 0, so a better point is live
                     alive = c > 0.0 ? alive : (alive & ~(1u << b));
                     bc = better ? c : bc;
-                    bk = better ? k : bk;
+                    be = better ? e : be;
                     if (!mm) break;
                     b = b2;
                 }
                 qi = i;
-                qbest = bk ? mkkey(bc, bk) : 0ull;
+                qbest = bc > 0.0 ? mkkey(bc, be) : 0ull;
             }
             if (qbest) atomicMax(&qkey[qi], qbest);
-            __syncthreads();
+            if (__syncthreads_or(lv == 0 && over)) {
+                state = 2;  // too many live points for a wave's compact part
+                break;
+            }
             // every wave reads the chords' keys: which chords found a point
             // (the same in every wave, so every thread takes the same exit)
             const int lane = L & 63;
@@ -437,10 +483,11 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                     sm.qS[nb][L + pre] = sm.qS[cb][L];
                     sm.qW[nb][L + pre] = sm.qW[cb][L];
                     if (kl) {
-                        const int k = (int)(0x1fff - (kl & 0x1fffull));
+                        const int e = (int)(0x1fff - (kl & 0x1fffull));
+                        const int k = cK[e];
                         sm.qk[nb][L + pre + 1] = k;
-                        sm.qS[nb][L + pre + 1] = pS[sk(k)];
-                        sm.qW[nb][L + pre + 1] = WT ? pW[sk(k)] : (double)k;
+                        sm.qS[nb][L + pre + 1] = cS[e];
+                        sm.qW[nb][L + pre + 1] = WT ? cW[e] : (double)k;
                     }
                 }
                 sm.qkey[(lv & 1) ^ 1][L] = 0ull;
@@ -455,8 +502,9 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 const unsigned long long kc = qkey[ci];
                 const int pre = __popcll(bal & ((1ull << ci) - 1ull));
                 if (kc) {
-                    const int k = (int)(0x1fff - (kc & 0x1fffull));
-                    const Pt K{WT ? pW[sk(k)] : (double)k, pS[sk(k)]};
+                    const int e = (int)(0x1fff - (kc & 0x1fffull));
+                    const int k = cK[e];
+                    const Pt K{WT ? cW[e] : (double)k, cS[e]};
                     if (k <= base) {
                         A = K;
                         ci += pre + 1;

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(NT) void k_short_rows(const T* __restrict__ y,
 
 
 template <bool WT, typename T, bool ST>
-__global__ __launch_bounds__(kLongNT, WT || sizeof(T) == 8 ? 2 : 4) void k_chunk_hulls(
+__global__ __launch_bounds__(kLongNT, WT ? 3 : sizeof(T) == 8 ? 4 : 5) void k_chunk_hulls(
     const T* __restrict__ y, const T* __restrict__ w, int64_t n, int m, float sign, LongWs ws,
     int full_slots) {
     __shared__ HullSmem<kLongNT, kLongP, WT, kHullQuick> sm;
