@@ -156,7 +156,10 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
 // the segment lists in the workspace.  Per level: one thread per merge finds its
 // bridge and cuts the two boundary segments in place; then teams of threads
 // move each right list's remaining descriptors down behind the left list's
-// (through a scratch copy, since the two ranges may overlap).
+// (through a scratch copy, since the two ranges may overlap).  The chunk
+// starts come from the first stage (group starts plus starts within groups);
+// at the end the root list and its prefix counts are left for the expansion,
+// which forms each chunk's record itself.
 // MODE: 0 the production instance, 1 with phase stamps, 2 with the debug checks
 // and schedule variants.
 template <bool WT, int MODE>
@@ -168,7 +171,6 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     __shared__ int sflag;
     __shared__ int s_nhard;
     __shared__ int4 s_hard[kHardCap];
-    constexpr int NW = NT / 64;
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m;
     const int tid = threadIdx.x;
@@ -184,53 +186,86 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     double* const STS = ws.st_S + rb;
     double* const STW = WT ? ws.st_W + rb : nullptr;
 
-    // ---- row flags, chunk starts (exclusive scan of the chunk totals)
+    // ---- row flags and group starts (an exclusive scan of the first stage's
+    // group totals), then every chunk start as its group's start plus its
+    // start within the group (both from the first stage)
+    const int ng = (m + kGroup - 1) / kGroup;
+    double* const gS = reinterpret_cast<double*>(MI);  // (the merge's scratch, free until the tree)
+    double* const gW = gS + ng;
     if (tid == 0) sflag = 0;
     __syncthreads();
     int f = 0;
-    for (int j = tid; j < m; j += NT) f |= ws.chunk_flag[rb + j] & kFlagData;
-    if (f) atomicOr(&sflag, f);
     double carryS = 0.0, carryW = 0.0;
-    for (int t0 = 0; t0 < m; t0 += NT) {
-        int j = t0 + tid;
-        double vs = j < m ? ws.tot_S[rb + j] : 0.0;
+    for (int g0 = 0; g0 < ng; g0 += NT) {
+        const int g = g0 + tid;
+        double2 t = make_double2(0.0, 0.0);
+        if (g < ng) {
+            const GroupWin* gw = ws.gwin + row * ng + g;
+            f |= gw->flags;
+            CNT[g * kGroup] = gw->nseg;  // the first stage's group lists: their segment counts
+            t = ws.gtot[row * ng + g];
+        }
         double tot;
-        double xs = wg_excl_scan<NT>(vs, red, &tot);
-        if (j < m) STS[j] = carryS + xs;
+        const double xs = wg_excl_scan<NT>(t.x, red, &tot);
+        if (g < ng) gS[g] = carryS + xs;
         carryS += tot;
         if (WT) {
-            double vw = j < m ? ws.tot_W[rb + j] : 0.0;
-            double xw = wg_excl_scan<NT>(vw, red, &tot);
-            if (j < m) STW[j] = carryW + xw;
+            const double xw = wg_excl_scan<NT>(t.y, red, &tot);
+            if (g < ng) gW[g] = carryW + xw;
             carryW += tot;
         }
     }
-    // the first stage's group lists: their segment counts
-    const int ng = (m + kGroup - 1) / kGroup;
-    for (int g = tid; g < ng; g += NT) CNT[g * kGroup] = ws.gwin[row * ng + g].nseg;
-    // warm this XCD's L2 with the compact hull ends of the whole row
-    {
-        const double2* wv = reinterpret_cast<const double2*>(ws.win + rb);
-        const int nv2 = m * (int)(sizeof(WinRec) / sizeof(double2));
-        double acc = 0.0;
-        for (int i = tid; i < nv2; i += NT) acc += wv[i].x;
-        keep(acc);
+    if (f) atomicOr(&sflag, f);
+    __syncthreads();
+    for (int j = tid; j < m; j += NT) {
+        const double2 c = ws.cst[rb + j];
+        STS[j] = gS[j / kGroup] + c.x;
+        if (WT) STW[j] = gW[j / kGroup] + c.y;
     }
     __syncthreads();
     if (tid == 0) ws.row_flag[row] = sflag;
+    stamp(sr, 1);  // prelude: flags, chunk starts, group list counts, windows read
 
     const size_t sl = (size_t)rb * (kChunk + 1);
     RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
               STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
 
     // ---- the merge tree's remaining levels (tree level r: span 2^r chunks)
-    for (int span = kGroup, r = 6; span < m; span <<= 1, ++r)
+    for (int span = kGroup, r = 6; span < m; span <<= 1, ++r) {
         merge_level<NT, EX>(X, D, SCR, CNT, MI, m, span, &s_nhard, s_hard, kHardCap,
                             MergeCtl{ws.sched, ws.dbg, r});
+        if (r - 6 < 11) stamp(sr, 5 + r - 6);  // through tree level r
+    }
 
     stamp(sr, 2);  // merge tree done
-    // ---- reconstruction records (Corollary 4.5)
-    write_records<NT>(X, D, CNT[0], m, ws.vb + rb, ws.rec + rb, ired);
+    // ---- what the expansion needs for its records (Corollary 4.5): the root
+    // list (into desc_scr), the root vertices before each segment (vb), and
+    // each chunk's first root segment (into node_cnt, no longer a count);
+    // each thread a run of consecutive segments, their chunks staged in the
+    // merge's scratch (merge_info) for the search
+    const int nroot = CNT[0];
+    int32_t* const rcg = reinterpret_cast<int32_t*>(MI);
+    {
+        const int ks = (nroot + NT - 1) / NT;
+        const int i0 = min(nroot, tid * ks), i1 = min(nroot, i0 + ks);
+        int loc = 0;
+        for (int i = i0; i < i1; ++i) {
+            const uint2 d = D[i];
+            SCR[i] = d;
+            rcg[i] = dchunk(d);
+            loc += dhi(d) - dlo(d) + 1;
+        }
+        int tot;
+        int x = wg_excl_scan_int<NT>(loc, ired, &tot);  // its barriers also publish rcg
+        for (int i = i0; i < i1; ++i) {
+            const uint2 d = D[i];
+            ws.vb[rb + i] = x;
+            x += dhi(d) - dlo(d) + 1;
+        }
+    }
+    __syncthreads();  // every thread has read CNT[0] before fs overwrites it
+    root_fs<NT>(nroot, m, CNT, rcg);
+    if (tid == 0) ws.root_n[row] = nroot;
     stamp(sr, 4);  // end
 }
 
@@ -894,14 +929,14 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
 // list, every part a stride of the vertices.
 constexpr int kDbgParts = 64;
 template <bool WT>
-__global__ __launch_bounds__(256) void k_debug_root(int m, LongWs ws, int two_stage) {
+__global__ __launch_bounds__(256) void k_debug_root(int m, LongWs ws) {
     const int64_t row = blockIdx.x / kDbgParts;
     const int part = (int)(blockIdx.x - row * kDbgParts);
     const int64_t rb = row * m;
     const int tid = threadIdx.x;
     if (ws.row_flag[row] & kFlagNonfinite) return;
-    const uint2* D = two_stage ? ws.desc_scr + rb : ws.desc + rb;
-    const int nroot = two_stage ? (ws.root_n[row] & ~kRootSlopes) : ws.node_cnt[rb];
+    const uint2* D = ws.desc_scr + rb;  // both merge paths leave the root list here
+    const int nroot = ws.root_n[row] & ~kRootSlopes;
     const int32_t* HC = ws.hull_cnt + rb;
     unsigned long long bad = 0;
     if (nroot < 1 || nroot > m) {
@@ -1004,7 +1039,7 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
     }
     // very long rows: one workgroup per row merges the group lists through the
     // remaining levels, lists in the workspace
-    *rec_done = true;
+    *rec_done = false;
     timed_begin(kPhaseMergeTop, st);
     if (wt)
         hipLaunchKernelGGL((k_merge_rows<true, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
@@ -1026,9 +1061,8 @@ hipError_t launch_segment_merge(const LongShape& sh, const LongWs& ws, hipStream
     else e = launch_segment_merge_t<0>(sh, ws, st, rec_done);
     if (e != hipSuccess || !ws.dbg) return e;
     const dim3 grid((unsigned)(sh.rows * kDbgParts));
-    const int two = two_stage_merge(sh.m) ? 1 : 0;
-    if (sh.weighted) hipLaunchKernelGGL(k_debug_root<true>, grid, dim3(256), 0, st, sh.m, ws, two);
-    else hipLaunchKernelGGL(k_debug_root<false>, grid, dim3(256), 0, st, sh.m, ws, two);
+    if (sh.weighted) hipLaunchKernelGGL(k_debug_root<true>, grid, dim3(256), 0, st, sh.m, ws);
+    else hipLaunchKernelGGL(k_debug_root<false>, grid, dim3(256), 0, st, sh.m, ws);
     return hipGetLastError();
 }
 
