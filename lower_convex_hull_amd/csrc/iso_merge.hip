@@ -38,20 +38,27 @@ struct MergeCtl {
 // counters, checks every merged list: at most one segment per chunk (node) of
 // its range, in strictly increasing order, each with lo <= hi (Definition 4.3,
 // Theorem 4.4).
+// The level's merges are k = 0 .. nm-1 (nm = merges_at(m, span)); this
+// workgroup runs merges kb .. ke-1 (all of them, or its share when a level is
+// spread over several workgroups: merges touch disjoint ranges of D).
+__host__ __device__ inline int merges_at(int m, int span) { return (m - span + 2 * span - 1) / (2 * span); }
+
 template <int NT, bool EX, class V, class DT>
 __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* CNT, int2* MI, int m, int span,
-                            int* s_nhard, int4* s_hard, int hard_cap, const MergeCtl ctl0) {
+                                            int kb, int ke, int* s_nhard, int4* s_hard, int hard_cap,
+                                            const MergeCtl ctl0) {
     // the schedule variants and the debug checks exist only in the EX instances
     const MergeCtl ctl = EX ? ctl0 : MergeCtl{0, nullptr, ctl0.r};
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, wid = tid >> 6, wlane = tid & 63;
-    const int nm = (m - span + 2 * span - 1) / (2 * span);
-    if (nm > NW && !(ctl.sched & kSchedWaveAll)) {
+    const int nm = merges_at(m, span);
+    const int nloc = ke - kb;
+    if (nloc > NW && !(ctl.sched & kSchedWaveAll)) {
         if (tid == 0) *s_nhard = 0;
         __syncthreads();
         const bool three = EX && (ctl.sched & kSchedThreeCase) != 0;
         const int cap = three ? 8 * (ctl.r + 12) : kWalkCap;  // log2 C = 12
-        for (int k = tid; k < nm; k += NT) {
+        for (int k = kb + tid; k < ke; k += NT) {
             const int a = 2 * k * span, b = a + span;
             List<DT> Lq{D + a, CNT[a]};
             List<DT> Rq{D + b, CNT[b]};
@@ -95,7 +102,7 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
             if (wlane == 0) apply_cut(D, CNT, MI, k, a, b, Rq.n, br);
         }
     } else {
-        for (int k = wid; k < nm; k += NW) {
+        for (int k = kb + wid; k < ke; k += NW) {
             const int a = 2 * k * span, b = a + span;
             List<DT> Lq{D + a, CNT[a]};
             List<DT> Rq{D + b, CNT[b]};
@@ -110,18 +117,18 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
         }
     }
     __syncthreads();
-    int ts = NT / nm;
+    int ts = NT / nloc;
     ts = ts < 1 ? 1 : (1 << (31 - __clz(ts)));
     const int teams = NT / ts;
     const int lane = tid & (ts - 1);
-    for (int k = tid / ts; k < nm; k += teams) {
+    for (int k = kb + tid / ts; k < ke; k += teams) {
         const int b = (2 * k + 1) * span;
         const int rs = MI[k].y;
         const int nr = CNT[b] - rs;
         for (int i = lane; i < nr; i += ts) SCR[b + i] = D[b + rs + i];
     }
     __syncthreads();
-    for (int k = tid / ts; k < nm; k += teams) {
+    for (int k = kb + tid / ts; k < ke; k += teams) {
         const int a = 2 * k * span, b = a + span;
         const int nl = MI[k].x;
         const int nr = CNT[b] - MI[k].y;
@@ -129,9 +136,11 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
     }
     __syncthreads();
     if (EX && ctl.dbg) {
-        // every node of the next level: a = 0, 2 span, ...
+        // the nodes of the next level this workgroup made (a = 2 span k), and
+        // the last workgroup also the unpaired node at the end, if any
         unsigned long long bad = 0;
-        for (int a = 2 * span * tid; a < m; a += 2 * span * NT) {
+        const int kl = ke == nm ? ke + 1 : ke;
+        for (int a = 2 * span * (kb + tid); a < m && a < 2 * span * kl; a += 2 * span * NT) {
             const int n = CNT[a], hi_node = min(m, a + 2 * span);
             if (n < 1 || n > hi_node - a) {
                 ++bad;
@@ -146,7 +155,7 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
             }
         }
         dbg_add(ctl.dbg, kDbgViolations, bad);
-        if (tid == 0) dbg_add(ctl.dbg, kDbgLevels);
+        if (tid == 0 && kb == 0) dbg_add(ctl.dbg, kDbgLevels);
     }
 }
 
@@ -162,8 +171,12 @@ __device__ __forceinline__ void merge_level(const V X, DT* D, DT* SCR, int32_t* 
 // which forms each chunk's record itself.
 // MODE: 0 the production instance, 1 with phase stamps, 2 with the debug checks
 // and schedule variants.
+// Launched twice per call: the prelude (kMergeRowsPre), then, after the levels
+// that k_merge_level spreads over workgroups, the remaining levels from span0
+// on and the end (kMergeRowsTail).
+constexpr int kMergeRowsPre = 1, kMergeRowsTail = 2;
 template <bool WT, int MODE>
-__global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
+__global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws, int span0, int phases) {
     constexpr bool ST = MODE == 1, EX = MODE == 2;
     constexpr int NT = kMergeNT;
     __shared__ double red[NT / 64 + 1];
@@ -177,7 +190,6 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     const int wid = tid >> 6, wlane = tid & 63;
 
     uint64_t* const sr = ST ? stamp_row(ws.st_top, row) : nullptr;
-    stamp(sr, 0);
     uint2* const D = ws.desc + rb;
     uint2* const SCR = ws.desc_scr + rb;
     int32_t* const CNT = ws.node_cnt + rb;
@@ -186,6 +198,11 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     double* const STS = ws.st_S + rb;
     double* const STW = WT ? ws.st_W + rb : nullptr;
 
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
+              STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
+    if (phases & kMergeRowsPre) {
+    stamp(sr, 0);
     // ---- row flags and group starts (an exclusive scan of the first stage's
     // group totals), then every chunk start as its group's start plus its
     // start within the group (both from the first stage)
@@ -224,15 +241,14 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     }
     __syncthreads();
     if (tid == 0) ws.row_flag[row] = sflag;
-    stamp(sr, 1);  // prelude: flags, chunk starts, group list counts, windows read
-
-    const size_t sl = (size_t)rb * (kChunk + 1);
-    RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb, HC,
-              STS, WT ? STW : nullptr, WT, inc_src(ws, row, m, 0)};
+    stamp(sr, 1);  // prelude: flags, chunk starts, group list counts
+    }
+    if (!(phases & kMergeRowsTail)) return;
+    stamp(sr, 3);  // the levels left to this kernel start
 
     // ---- the merge tree's remaining levels (tree level r: span 2^r chunks)
-    for (int span = kGroup, r = 6; span < m; span <<= 1, ++r) {
-        merge_level<NT, EX>(X, D, SCR, CNT, MI, m, span, &s_nhard, s_hard, kHardCap,
+    for (int span = span0, r = 31 - __clz(span0); span < m; span <<= 1, ++r) {
+        merge_level<NT, EX>(X, D, SCR, CNT, MI, m, span, 0, merges_at(m, span), &s_nhard, s_hard, kHardCap,
                             MergeCtl{ws.sched, ws.dbg, r});
         if (r - 6 < 11) stamp(sr, 5 + r - 6);  // through tree level r
     }
@@ -269,6 +285,28 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_rows(int m, LongWs ws) {
     stamp(sr, 4);  // end
 }
 
+
+// One level of the merge tree of rows beyond the two-stage merge, spread over
+// workgroups (grid: workgroups per row, rows): workgroup x runs merges
+// x*per .. x*per+per-1 of its row, a wave per merge when per is at most the
+// workgroup's waves.
+template <bool WT, int MODE>
+__global__ __launch_bounds__(kMergeNT) void k_merge_level(int m, int span, int per, LongWs ws) {
+    constexpr bool EX = MODE == 2;
+    constexpr int NT = kMergeNT;
+    __shared__ int s_nhard;
+    __shared__ int4 s_hard[kHardCap];
+    const int64_t row = blockIdx.y;
+    const int64_t rb = row * m;
+    const int nm = merges_at(m, span);
+    const int kb = (int)blockIdx.x * per, ke = min(nm, kb + per);
+    if (kb >= ke) return;  // (the same in every thread)
+    const size_t sl = (size_t)rb * (kChunk + 1);
+    const RowView X{ws.slot_idx + sl, ws.slot_S + sl, WT ? ws.slot_W + sl : nullptr, ws.win + rb,
+                    ws.hull_cnt + rb, ws.st_S + rb, WT ? ws.st_W + rb : nullptr, WT, inc_src(ws, row, m, 0)};
+    merge_level<NT, EX>(X, ws.desc + rb, ws.desc_scr + rb, ws.node_cnt + rb, ws.merge_info + rb, m, span, kb, ke,
+                        &s_nhard, s_hard, kHardCap, MergeCtl{ws.sched, ws.dbg, 31 - __clz(span)});
+}
 
 // Vertices of group hulls for the second stage: position p of group g's hull,
 // relative to group gr's first point.
@@ -509,7 +547,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
             __syncthreads();
         } else {
             for (int span = 1; span < gc; span <<= 1)
-                merge_level<NT, EX>(X, D, SCR, CNT, MI, gc, span, &s_nhard, s_hard, G / 2,
+                merge_level<NT, EX>(X, D, SCR, CNT, MI, gc, span, 0, merges_at(gc, span), &s_nhard, s_hard, G / 2,
                                     MergeCtl{ws.sched, ws.dbg, 31 - __clz(span)});
         }
         stamp(sr, 2);  // merge tree done (segment lists)
@@ -798,7 +836,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             __syncthreads();
         } else {
             for (int span = 1; span < ng; span <<= 1)
-                merge_level<NT, EX>(X, D, SCR, CNT, MI, ng, span, &s_nhard, s_hard, kHardCap,
+                merge_level<NT, EX>(X, D, SCR, CNT, MI, ng, span, 0, merges_at(ng, span), &s_nhard, s_hard, kHardCap,
                                     MergeCtl{ws.sched, ws.dbg, 6 + 31 - __clz(span)});
         }
         stamp(sr, 2);  // merge tree done (segment lists)
@@ -1039,12 +1077,26 @@ hipError_t launch_segment_merge_t(const LongShape& sh, const LongWs& ws, hipStre
     }
     // very long rows: one workgroup per row merges the group lists through the
     // remaining levels, lists in the workspace
+    // very long rows: the prelude, then the levels with more merges than a
+    // workgroup has waves over several workgroups (a wave per merge), then
+    // one workgroup per row for the last levels and the end
     *rec_done = false;
     timed_begin(kPhaseMergeTop, st);
+    constexpr int per = kMergeNT / 64;
     if (wt)
-        hipLaunchKernelGGL((k_merge_rows<true, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<true, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws, sh.m, kMergeRowsPre);
     else
-        hipLaunchKernelGGL((k_merge_rows<false, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws);
+        hipLaunchKernelGGL((k_merge_rows<false, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws, sh.m, kMergeRowsPre);
+    int span = kGroup;
+    for (; span < sh.m && merges_at(sh.m, span) > per; span <<= 1) {
+        const dim3 grid((unsigned)((merges_at(sh.m, span) + per - 1) / per), R);
+        if (wt) hipLaunchKernelGGL((k_merge_level<true, MODE>), grid, dim3(kMergeNT), 0, st, sh.m, span, per, ws);
+        else hipLaunchKernelGGL((k_merge_level<false, MODE>), grid, dim3(kMergeNT), 0, st, sh.m, span, per, ws);
+    }
+    if (wt)
+        hipLaunchKernelGGL((k_merge_rows<true, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws, span, kMergeRowsTail);
+    else
+        hipLaunchKernelGGL((k_merge_rows<false, MODE>), dim3(R), dim3(kMergeNT), 0, st, sh.m, ws, span, kMergeRowsTail);
     timed_end(st);
     return hipGetLastError();
 }
