@@ -215,6 +215,8 @@ def extras(b, args, np):
     y, w = inputs.config("c5_calib256x2p20")
     yt, wt = dev_t(y), dev_t(w)
     run_fit("c5_calib256x2p20", yt, wt, "256 x 2^20, f32, integer-count weights")
+    if args.cpu_seconds > 0:
+        out["c5_calib256x2p20"]["cpu_oracle_all_cores"] = cpu_rows_all_cores(y, w, args.cpu_seconds)
 
     # backward pass on the calibration batch: d/dy and d/dw
     st, bid = None, torch.empty(yt.shape, dtype=torch.int32, device=dev)
@@ -365,6 +367,33 @@ def phase_stamps(b, y, calls=5):
                       "median_per_workgroup_us": {k: round(float(np.median(v)), 2) for k, v in d.items()
                                                   if k not in ("span_us", "wg")}}
     return res
+
+
+def cpu_rows_all_cores(y, w, seconds):
+    """The oracle on the host cores, rows spread over a thread pool (the C
+    oracle runs with the interpreter lock released), over a bounded sample of
+    the batch's rows: elements per second and the threads used."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rows = y.shape[0]
+    t0 = time.perf_counter()
+    oracle.fit_rows_f32(y[:1], None if w is None else w[:1])
+    per_row = max(time.perf_counter() - t0, 1e-6)
+    take = int(min(rows, max(cores, seconds * cores / per_row / 4)))
+    take -= take % cores if take >= cores else 0
+
+    def one(r):
+        oracle.fit_rows_f32(y[r:r + 1], None if w is None else w[r:r + 1])
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(one, range(take)))
+    t = time.perf_counter() - t0
+    return {"value": take * y.shape[1] / t, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"{take} of the batch's {rows} rows, one row per task on {cores} threads, {t:.2f} s"}
 
 
 def copy_ceiling(b, K):
