@@ -124,7 +124,10 @@ enum {
      * Slots: chunk 0 start, 1 loads/sums/scan, 5 first quickhull level, 2 hull
      * built, 4 end; merge stages 0 start, 1 prelude, 2 merge tree, 3 lists and
      * windows written, 4 end, 5 + l node 0 through level l of a compact
-     * merge tree; expansion 0 start, 1 record ready, 4 end. */
+     * merge tree; expansion 0 start, 1 record ready, 4 end.  Rows beyond the
+ * two-stage merge use the second-stage row for the row merge: 0 start, 1
+ * prelude done, 3 start of the levels left to one workgroup, 5 + (r - 6)
+ * through tree level r, 2 tree done, 4 end. */
     ISO_F_PHASE_STAMPS = 0x200u,
     /* Merge-schedule variants (measurement and stress; paper section 7.4 and
      * appendix A).  Same result.  WAVE_MERGES: every merge of a segment-list
