@@ -474,7 +474,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             }
             if (L < 64) {
                 // wave 0 writes the new list, each chord's point after the
-                // chord's start (coordinates from the staged points), and
+                // chord's start (coordinates from the compact arrays), and
                 // clears the other key buffer (last read a level ago)
                 const int pre = __popcll(bal & ((1ull << L) - 1ull));
                 const int nb = 1 - cb;
