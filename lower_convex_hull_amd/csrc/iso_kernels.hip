@@ -440,7 +440,16 @@ hipError_t launch_short(const T* y, const T* w, int64_t rows, int64_t n, float s
     if (n <= 128) return launch_short_t<64, 2>(y, w, rows, n, sign, out, block_id, row_flag, st);
     if (n <= 256) return launch_short_t<64, 4>(y, w, rows, n, sign, out, block_id, row_flag, st);
     if (n <= 512) return launch_short_t<64, 8>(y, w, rows, n, sign, out, block_id, row_flag, st);
-    if (n <= 1024) return launch_short_t<64, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    // a batch too small to fill the GPU with one wave (or four) per row gets
+    // four times (twice) as many threads per row, each with fewer points:
+    // shorter per-thread loops on the row's latency chain; a large batch keeps
+    // the narrower workgroups, which do less work per row
+    constexpr int64_t kFillWaves = 8192;  // waves the GPU holds at once (256 CUs x 32)
+    if (n <= 1024) {
+        if (rows * 4 <= kFillWaves) return launch_short_t<256, 4>(y, w, rows, n, sign, out, block_id, row_flag, st);
+        return launch_short_t<64, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
+    }
+    if (rows * 8 <= kFillWaves) return launch_short_t<512, 8>(y, w, rows, n, sign, out, block_id, row_flag, st);
     return launch_short_t<256, 16>(y, w, rows, n, sign, out, block_id, row_flag, st);
 }
 

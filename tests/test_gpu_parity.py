@@ -166,6 +166,20 @@ def test_ragged_sizes(torch, n):
     check(torch, y, w, name=f"ragged-w/{n}")
 
 
+def test_short_row_shapes_by_batch_size(torch):
+    """Short rows take wider workgroups when the batch is too small to fill the
+    GPU and the narrower ones otherwise: both shapes on each side of the
+    switch (rows*4 or rows*8 waves against 8192), unit and integer weights."""
+    cases = [(2048, 700, "noisy"), (2049, 700, "noisy"), (1024, 2000, "noisy"), (1025, 2000, "noisy"),
+             (2049, 1024, "calibration"), (1025, 4096, "calibration")]
+    for rows, n, kind in cases:
+        if kind == "noisy":
+            y, w = inputs.noisy(rows, n, rows + n)
+        else:
+            y, w = inputs.calibration(rows, n, rows + n)
+        check(torch, y, w, name=f"short shapes {kind} {rows}x{n}", block_ids=rows * n <= 3_000_000)
+
+
 def test_batch_of_long_rows(torch):
     y, w = inputs.calibration(6, 20_000, 77)
     check(torch, y, w, name="long-batch")
