@@ -27,7 +27,7 @@ namespace {
 constexpr int kVjpNT = 256;
 constexpr int kVjpP = 8;
 constexpr int kVjpT = kVjpNT * kVjpP;  // elements of a tile
-constexpr int kCarryNT = 1024;
+constexpr int kCarryBlk = 256;  // tiles per workgroup of the carry kernels
 
 // Boundary record of one tile of a long row: where its first and last block
 // starts lie and the sums (g, w, w*y) over the stretch before the first start
@@ -46,6 +46,15 @@ struct VjpRec {
 struct VjpTot {
     double F[3];
     double L[3];
+};
+
+// A block of kCarryBlk tiles reduced: its forward value over the tails and its
+// backward value over the heads (segmented: see phase 2).
+struct CarryAgg {
+    double fv[3];
+    double bv[3];
+    int32_t ff, bf;
+    int32_t pad[2];
 };
 
 struct Sums {
@@ -368,80 +377,132 @@ __global__ __launch_bounds__(kVjpNT) void k_vjp_tiles(const T* __restrict__ g, c
 // that lies in earlier tiles and Q_t the part of the block open at its end
 // that lies in later tiles (segmented scans over the tiles, forward of the
 // tails and backward of the heads): F_t = P_t + head_t (+ Q_t when the tile
-// holds no start) and L_t = tail_t + Q_t.
-__global__ __launch_bounds__(kCarryNT) void k_vjp_carry(const VjpRec* __restrict__ rec, int mt,
-                                                        VjpTot* __restrict__ tot) {
-    constexpr int NT = kCarryNT;
+// holds no start) and L_t = tail_t + Q_t.  The scans run over many
+// workgroups: each takes kCarryBlk consecutive tiles; k_vjp_agg reduces its
+// tiles to one forward and one backward value, and k_vjp_apply folds the
+// values of the blocks before (after) it, then scans its own tiles.  (A
+// segmented value (f, v): v is the sum since the nearest tile holding a start,
+// in scan order, that tile's own value included; f whether there is one.)
+
+// One tile's boundary record (zero sums, no start, past the row's end).
+__device__ __forceinline__ void load_carry_tile(const VjpRec* __restrict__ rec, int t, int mt, bool& f, Sums& tl,
+                                                Sums& hd) {
+    const VjpRec r = rec[min(t, mt - 1)];
+    const bool in = t < mt;
+    f = in && r.has != 0;
+    tl = in ? Sums{r.tail[0], r.tail[1], r.tail[2]} : Sums{0.0, 0.0, 0.0};
+    hd = in ? Sums{r.head[0], r.head[1], r.head[2]} : Sums{0.0, 0.0, 0.0};
+}
+
+// The inclusive value of the last thread in scan order, from an exclusive scan.
+__device__ __forceinline__ void seg_fold(bool fx, Sums vx, bool f, Sums v, bool& fo, Sums& vo) {
+    fo = fx || f;
+    vo = f ? v : vx + v;
+}
+
+__global__ __launch_bounds__(kCarryBlk) void k_vjp_agg(const VjpRec* __restrict__ rec, int mt, int nb,
+                                                       CarryAgg* __restrict__ agg) {
+    constexpr int NT = kCarryBlk;
     __shared__ int sf[NT / 64];
     __shared__ Sums sv[NT / 64];
-    __shared__ int s_cf;
-    __shared__ Sums s_cv;
-    const int64_t rb = (int64_t)blockIdx.x * mt;
-    const int tid = threadIdx.x;
-    // forward: P_t
-    bool cf = false;
-    Sums cv{0.0, 0.0, 0.0};
-    for (int t0 = 0; t0 < mt; t0 += NT) {
-        const int t = t0 + tid;
-        bool f = false;
-        Sums v{0.0, 0.0, 0.0}, h{0.0, 0.0, 0.0};
-        if (t < mt) {
-            const VjpRec r = rec[rb + t];
-            f = r.has != 0;
-            v = Sums{r.tail[0], r.tail[1], r.tail[2]};
-            h = Sums{r.head[0], r.head[1], r.head[2]};
+    const int64_t row = blockIdx.x;  // (grid: rows, blocks per row)
+    const int t = (int)blockIdx.y * NT + (int)threadIdx.x;
+    bool f;
+    Sums tl, hd;
+    load_carry_tile(rec + row * mt, t, mt, f, tl, hd);
+    bool fx;
+    Sums vx;
+    wg_seg_scan_excl<NT, true>(f, tl, sf, sv, fx, vx);
+    CarryAgg* a = agg + row * nb + blockIdx.y;
+    if (threadIdx.x == NT - 1) {
+        bool fo;
+        Sums vo;
+        seg_fold(fx, vx, f, tl, fo, vo);
+        a->ff = fo ? 1 : 0;
+        a->fv[0] = vo.a; a->fv[1] = vo.b; a->fv[2] = vo.c;
+    }
+    wg_seg_scan_excl<NT, false>(f, hd, sf, sv, fx, vx);
+    if (threadIdx.x == 0) {
+        bool fo;
+        Sums vo;
+        seg_fold(fx, vx, f, hd, fo, vo);
+        a->bf = fo ? 1 : 0;
+        a->bv[0] = vo.a; a->bv[1] = vo.b; a->bv[2] = vo.c;
+    }
+}
+
+__global__ __launch_bounds__(kCarryBlk) void k_vjp_apply(const VjpRec* __restrict__ rec,
+                                                         const CarryAgg* __restrict__ agg, int mt, int nb,
+                                                         VjpTot* __restrict__ tot) {
+    constexpr int NT = kCarryBlk;
+    __shared__ int sf[NT / 64];
+    __shared__ Sums sv[NT / 64];
+    __shared__ Sums s_in[2];
+    const int64_t row = blockIdx.x;  // (grid: rows, blocks per row)
+    const int b = (int)blockIdx.y;
+    const int t = b * NT + (int)threadIdx.x;
+    bool f;
+    Sums tl, hd;
+    load_carry_tile(rec + row * mt, t, mt, f, tl, hd);
+    // the values carried into this block: the blocks before it (forward) and
+    // after it (backward), folded in rounds of NT blocks
+    const CarryAgg* ar = agg + row * nb;
+    Sums pin{0.0, 0.0, 0.0}, qin{0.0, 0.0, 0.0};
+    for (int k0 = 0; k0 < b; k0 += NT) {  // blocks k0 .. min(b, k0+NT)-1, in order
+        const int k = k0 + (int)threadIdx.x;
+        bool af = false;
+        Sums av{0.0, 0.0, 0.0};
+        if (k < b) {
+            af = ar[k].ff != 0;
+            av = Sums{ar[k].fv[0], ar[k].fv[1], ar[k].fv[2]};
         }
         bool fx;
         Sums vx;
-        wg_seg_scan_excl<NT, true>(f, v, sf, sv, fx, vx);
-        const Sums p = fx ? vx : cv + vx;  // with the carry of earlier blocks of tiles
-        if (t < mt) {
-            const Sums F = p + h;
-            tot[rb + t].F[0] = F.a; tot[rb + t].F[1] = F.b; tot[rb + t].F[2] = F.c;
-        }
-        // the carry into the next block of tiles: the last tile's inclusive value
-        if (tid == NT - 1) {  // tiles past mt add nothing, so this is the block's end
-            s_cf = (cf || fx || f) ? 1 : 0;
-            s_cv = f ? v : p + v;
+        wg_seg_scan_excl<NT, true>(af, av, sf, sv, fx, vx);
+        if (threadIdx.x == NT - 1) {  // blocks past b add nothing
+            bool fo;
+            Sums vo;
+            seg_fold(fx, vx, af, av, fo, vo);
+            s_in[0] = fo ? vo : pin + vo;
         }
         __syncthreads();
-        cf = s_cf != 0;
-        cv = s_cv;
+        pin = s_in[0];
         __syncthreads();
     }
-    // backward: Q_t (each tile on the thread that wrote its F above)
-    cf = false;
-    cv = Sums{0.0, 0.0, 0.0};
-    const int nb = (mt + NT - 1) / NT;
-    for (int k = nb - 1; k >= 0; --k) {
-        const int t = k * NT + tid;
-        bool f = false;
-        Sums v{0.0, 0.0, 0.0}, tl{0.0, 0.0, 0.0};
-        if (t < mt) {
-            const VjpRec r = rec[rb + t];
-            f = r.has != 0;
-            v = Sums{r.head[0], r.head[1], r.head[2]};
-            tl = Sums{r.tail[0], r.tail[1], r.tail[2]};
+    for (int k1 = nb - 1; k1 > b; k1 -= NT) {  // blocks max(b+1, k1-NT+1) .. k1, in reverse
+        const int k = k1 - (NT - 1) + (int)threadIdx.x;
+        bool af = false;
+        Sums av{0.0, 0.0, 0.0};
+        if (k > b) {
+            af = ar[k].bf != 0;
+            av = Sums{ar[k].bv[0], ar[k].bv[1], ar[k].bv[2]};
         }
         bool fx;
         Sums vx;
-        wg_seg_scan_excl<NT, false>(f, v, sf, sv, fx, vx);
-        const Sums q = fx ? vx : cv + vx;
-        if (t < mt) {
-            const Sums Lt = tl + q;
-            tot[rb + t].L[0] = Lt.a; tot[rb + t].L[1] = Lt.b; tot[rb + t].L[2] = Lt.c;
-            if (!f) {
-                tot[rb + t].F[0] += q.a; tot[rb + t].F[1] += q.b; tot[rb + t].F[2] += q.c;
-            }
-        }
-        if (tid == 0) {
-            s_cf = (cf || fx || f) ? 1 : 0;
-            s_cv = f ? v : q + v;
+        wg_seg_scan_excl<NT, false>(af, av, sf, sv, fx, vx);
+        if (threadIdx.x == 0) {  // blocks at or before b add nothing
+            bool fo;
+            Sums vo;
+            seg_fold(fx, vx, af, av, fo, vo);
+            s_in[1] = fo ? vo : qin + vo;
         }
         __syncthreads();
-        cf = s_cf != 0;
-        cv = s_cv;
+        qin = s_in[1];
         __syncthreads();
+    }
+    // this block's tiles
+    bool fx;
+    Sums vx;
+    wg_seg_scan_excl<NT, true>(f, tl, sf, sv, fx, vx);
+    const Sums P = fx ? vx : pin + vx;
+    wg_seg_scan_excl<NT, false>(f, hd, sf, sv, fx, vx);
+    const Sums Qv = fx ? vx : qin + vx;
+    if (t < mt) {
+        const Sums F = f ? P + hd : P + hd + Qv;
+        const Sums Lt = tl + Qv;
+        VjpTot* o = tot + row * mt + t;
+        o->F[0] = F.a; o->F[1] = F.b; o->F[2] = F.c;
+        o->L[0] = Lt.a; o->L[1] = Lt.b; o->L[2] = Lt.c;
     }
 }
 
@@ -481,6 +542,8 @@ struct VjpPlan {
     int64_t tiles = 0;
     size_t bytes = 0;
     size_t off_tot = 0;
+    int nb = 0;           // blocks of kCarryBlk tiles per row (long rows)
+    size_t off_agg = 0;
 };
 
 bool vjp_plan(int64_t rows, int64_t n, VjpPlan* p) {
@@ -501,7 +564,11 @@ bool vjp_plan(int64_t rows, int64_t n, VjpPlan* p) {
     p->tiles = mt * rows;
     const size_t rb = ((size_t)p->tiles * sizeof(VjpRec) + 255) / 256 * 256;
     p->off_tot = rb;
-    p->bytes = rb + (size_t)p->tiles * sizeof(VjpTot);
+    if ((mt + kCarryBlk - 1) / kCarryBlk > 65535) return false;  // blocks of a row: the grid's y extent
+    p->nb = (int)((mt + kCarryBlk - 1) / kCarryBlk);
+    const size_t tb = ((size_t)p->tiles * sizeof(VjpTot) + 255) / 256 * 256;
+    p->off_agg = rb + tb;
+    p->bytes = p->off_agg + (size_t)rows * p->nb * sizeof(CarryAgg);
     return true;
 }
 
@@ -517,7 +584,10 @@ hipError_t launch_vjp_t(const T* g, const T* y, const T* w, const int32_t* bid, 
     VjpTot* tot = reinterpret_cast<VjpTot*>(static_cast<char*>(ws) + p.off_tot);
     hipLaunchKernelGGL((k_vjp_tiles<T, WT, GW, false>), dim3((unsigned)p.tiles), dim3(kVjpNT), 0, st, g, y,
                        w, bid, rows, n, p.mt, 0, gy, gw, rec);
-    hipLaunchKernelGGL(k_vjp_carry, dim3((unsigned)rows), dim3(kCarryNT), 0, st, rec, p.mt, tot);
+    CarryAgg* agg = reinterpret_cast<CarryAgg*>(static_cast<char*>(ws) + p.off_agg);
+    const dim3 cg((unsigned)rows, (unsigned)p.nb);
+    hipLaunchKernelGGL(k_vjp_agg, cg, dim3(kCarryBlk), 0, st, rec, p.mt, p.nb, agg);
+    hipLaunchKernelGGL(k_vjp_apply, cg, dim3(kCarryBlk), 0, st, rec, agg, p.mt, p.nb, tot);
     hipLaunchKernelGGL((k_vjp_edges<T, WT, GW>), dim3((unsigned)p.tiles), dim3(kVjpNT), 0, st, y, w, n,
                        p.mt, rec, tot, gy, gw);
     return hipGetLastError();

@@ -130,6 +130,17 @@ def test_vjp_c4_dense_is_identity(torch):
     assert st == 0 and np.array_equal(gy, g)
 
 
+def test_vjp_one_block_over_several_carry_rounds(torch):
+    """A strictly decreasing row of 9e6 elements is one block spanning more
+    tiles than one round of the carry kernel holds (4096 tiles of 2048): the
+    block's sums cross the rounds in both directions; weighted, with d/dw."""
+    n = 9_000_000
+    rng = np.random.default_rng(41)
+    y = -np.sort(rng.random(n)).astype(np.float32)[None, :]
+    w = (0.5 + rng.random((1, n))).astype(np.float32)
+    full(torch, y, w, "one block 9e6", 41, own_blocks=True)
+
+
 def test_vjp_c5_full_batch(torch):
     """The 256 x 2^20 calibration batch, weighted: d/dy and d/dw of every row."""
     y, w = inputs.config("c5_calib256x2p20")
