@@ -675,16 +675,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
         const int i = tid + q * NT;
         raw[q] = i < nraw ? wsrc[i] : make_double2(0.0, 0.0);
     }
-    // the chunk starts relative to their groups (S only: unit weights), for
-    // the row's chunk starts stored at the end (a row has at most kTopMax
-    // groups of kGroup chunks)
     constexpr int kRo = (kTopMax * kGroup + NT - 1) / NT;
-    double cstv[kRo];
-#pragma unroll
-    for (int q = 0; q < kRo; ++q) {
-        const int j = tid + q * NT;
-        if (!WT && j < m) cstv[q] = reinterpret_cast<const double*>(ws.cst + rb + j)[0];
-    }
     const int wid = tid >> 6, lane = tid & 63;
     double2 gt0 = make_double2(0.0, 0.0), gt1 = make_double2(0.0, 0.0);  // groups 2*lane, 2*lane+1
     if (wid == 0) {
@@ -729,6 +720,16 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     }
     const bool fast = (__syncthreads_and(ok) != 0) && ng <= kTopFastMax && m < kTagMaxChunks;
     stamp(sr, 1);  // prelude loaded, group starts scanned
+    // the chunk starts relative to their groups (S only: unit weights), for
+    // the row's chunk starts stored at the end (a row has at most kTopMax
+    // groups of kGroup chunks): read now, behind the prelude's reads, while
+    // the merges work in LDS
+    double cstv[kRo];
+#pragma unroll
+    for (int q = 0; q < kRo; ++q) {
+        const int j = tid + q * NT;
+        if (!WT && j < m) cstv[q] = reinterpret_cast<const double*>(ws.cst + rb + j)[0];
+    }
     uint2* R = ws.desc_scr + rb;  // the root list, as segments of chunk hulls
     // after both paths' LDS: the root segments' chunks (and, on the compact
     // path, their vertex prefix), for the record prefix counts
