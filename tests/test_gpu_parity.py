@@ -245,6 +245,19 @@ def test_row_beyond_two_stage_merge(torch):
     check(torch, y, None, name="noisy/2.5e7", block_ids=False)
 
 
+def test_batch_of_rows_beyond_two_stage_merge(torch):
+    """Three rows beyond the two-stage merge in one call (weighted, block ids
+    checked): the row merge's tree levels spread over workgroups of every row
+    at once (grid rows x workgroups), and the records formed by the expansion
+    from each row's root list."""
+    n = 80 * 64 * 4096 + 7
+    y, _ = inputs.noisy(3, n, 35)
+    w = inputs.weights("uniform", 3 * n, 35).reshape(3, n)
+    y[1] = np.sort(y[1])  # a strictly increasing stretch ...
+    y[1, n // 3] = -5.0   # ... with a cliff: bridges reach across groups
+    check(torch, y, w, name="3 rows beyond two stages", block_ids=True)
+
+
 def test_rows_of_1e8(torch):
     """Rows of 10^8 elements (the paper's longest rows, Tables 1-3): beyond the
     two-stage merge, the groups' lists are merged through the remaining levels
