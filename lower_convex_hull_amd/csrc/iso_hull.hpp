@@ -343,10 +343,11 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             sm.qkey[0][L] = 0ull;
             sm.qkey[1][L] = 0ull;
         }
-        // this thread's chord, the one over point base (vertex ci <= base <
-        // vertex ci+1): its ends A, B and B's index kB, kept in registers from
-        // level to level; the list's size nv and buffer cb (the same in every
-        // thread); the keys of a level in buffer lv & 1
+        // this thread's chord, the one over its reference point (base in the
+        // first level, kref after it: vertex ci <= reference < vertex ci+1):
+        // its ends A, B and B's index kB, kept in registers from level to
+        // level; the list's size nv and buffer cb (the same in every thread);
+        // the keys of a level in buffer lv & 1
         int ci = 0, kB = len, nv = 2, cb = 0, state = 0;
         Pt A{0.0, 0.0}, B{sm.end_w, sm.end_s};
         // level 0 has one chord, from point 0 to point len: the thread's own
@@ -369,8 +370,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
         // in point order; this thread's start e0 there comes from a scan of
         // the live counts over the wave.  A wave with more than CW live points
         // stores nothing and the block falls back.
-        const uint32_t alive0 = alive;
-        int e0, over;
+        int e0, over, wtot;
         {
             const int lane = L & 63;
             const int cnt = __popc(alive);
@@ -381,7 +381,8 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 if (lane >= d) inc += t;
             }
             e0 = (L >> 6) * CW + inc - cnt;
-            over = __shfl(inc, 63) > CW;
+            wtot = __shfl(inc, 63);
+            over = wtot > CW;
             if (!over && alive) {
 #pragma unroll
                 for (int b = 0; b < P; ++b) {
@@ -398,7 +399,18 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 qbest0 = (qbest0 & ~0x1fffull) | (unsigned long long)(0x1fff - (e0 + __popc(alive & ((1u << b) - 1u))));
             }
         }
+        // from here on a lane works on an even share of its wave's live
+        // points: entries e_lo .. e_lo + nloc - 1 of the wave's compact part
+        // (the later levels' loops run as long as their wave's most loaded
+        // lane, and live points cluster near the hull), with kref the index
+        // just before its first point in place of the thread's own base
+        const int per = (wtot + 63) >> 6;
+        const int lo = min(wtot, (L & 63) * per);
+        const int nloc = min(wtot, lo + per) - lo;
+        const int e_lo = (L >> 6) * CW + lo;
+        alive = nloc > 0 && !over ? (1u << nloc) - 1u : 0u;
         __syncthreads();
+        const int kref = alive ? (int)cK[e_lo] - 1 : 0;
         for (int lv = 0; lv < kQhLevels; ++lv) {
             unsigned long long* qkey = sm.qkey[lv & 1];
             const int32_t* vk = sm.qk[cb];
@@ -418,17 +430,19 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 double Aw = A.w, As = A.s, dW = B.w - A.w, dS = B.s - A.s;
                 uint32_t mm = alive;
                 int b = lsb32(mm);
-                int en = e0 + __popc(alive0 & ((1u << b) - 1u));
+                int en = e_lo + b;
                 double Sn = cS[en];
                 double Wn = WT ? cW[en] : 0.0;
+                int kn = cK[en];
                 for (;;) {
-                    const int k = base + b + 1, e = en;
+                    const int k = kn, e = en;
                     const double Sk = Sn, Wk = WT ? Wn : (double)k;
                     mm &= mm - 1u;
                     const int b2 = mm ? lsb32(mm) : b;
-                    en = e0 + __popc(alive0 & ((1u << b2) - 1u));
+                    en = e_lo + b2;
                     Sn = cS[en];
                     if (WT) Wn = cW[en];
+                    kn = cK[en];
                     if (k >= nk) {
                         if (bc > 0.0) atomicMax(&qkey[i], mkkey(bc, be));
                         bc = 0.0;
@@ -498,14 +512,14 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             }
             if (alive) {
                 // this thread's chord in the new list: the half of the old
-                // one that holds point base
+                // one that holds point kref
                 const unsigned long long kc = qkey[ci];
                 const int pre = __popcll(bal & ((1ull << ci) - 1ull));
                 if (kc) {
                     const int e = (int)(0x1fff - (kc & 0x1fffull));
                     const int k = cK[e];
                     const Pt K{WT ? cW[e] : (double)k, cS[e]};
-                    if (k <= base) {
+                    if (k <= kref) {
                         A = K;
                         ci += pre + 1;
                     } else {
