@@ -45,15 +45,17 @@ struct HullSmem {
     int ired[NT / 64 + 1];
     double end_s, end_w;          // S and W of point len (padding points repeat it)
     int flag;
-    // quickhull: the points still live after the first level, compacted per
-    // wave in point order (S, W when weighted, and the block index; CW entries
-    // per wave; the region arrays serve where they exist), the vertex list
+    // quickhull: the points still live after the first level, compacted over
+    // the workgroup in point order (S, W when weighted, and the block index;
+    // room for CW entries per wave; the region arrays serve where they
+    // exist), each wave's count of them, the vertex list
     // (two buffers), and per chord the key of the farthest point below it
     static constexpr int CW = MODE == kHullQuick ? kQhWaveCap : 64 * RS;
     static constexpr int NC = MODE == kHullQuick ? (NT / 64) * kQhWaveCap : 1;
     double cS[NC];
     double cW[WT ? NC : 1];
     uint16_t ck[NC];
+    int32_t wcnt[NT / 64];
     int32_t qk[2][NQ];
     double qS[2][NQ], qW[2][NQ];
     unsigned long long qkey[2][NQ];
@@ -366,13 +368,14 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 qbest0 = key > qbest0 ? key : qbest0;
             }
         }
-        // the points still live go to the wave's part of the compact arrays,
-        // in point order; this thread's start e0 there comes from a scan of
-        // the live counts over the wave.  A wave with more than CW live points
-        // stores nothing and the block falls back.
+        // the points still live go to the compact arrays in point order; this
+        // thread's start e0 there comes from a scan of the live counts over
+        // the wave and the counts of the waves before it.  With more live
+        // points than the arrays hold nothing is stored and the block falls
+        // back.
         int e0, over, wtot;
         {
-            const int lane = L & 63;
+            const int lane = L & 63, wid = L >> 6;
             const int cnt = __popc(alive);
             int inc = cnt;
 #pragma unroll
@@ -380,9 +383,18 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 const int t = __shfl_up(inc, d);
                 if (lane >= d) inc += t;
             }
-            e0 = (L >> 6) * CW + inc - cnt;
-            wtot = __shfl(inc, 63);
-            over = wtot > CW;
+            if (lane == 63) sm.wcnt[wid] = inc;
+            __syncthreads();
+            int woff = 0;
+            wtot = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) {
+                const int c = sm.wcnt[w];
+                woff += w < wid ? c : 0;
+                wtot += c;
+            }
+            e0 = woff + inc - cnt;
+            over = wtot > (NT / 64) * CW;
             if (!over && alive) {
 #pragma unroll
                 for (int b = 0; b < P; ++b) {
@@ -399,15 +411,15 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                 qbest0 = (qbest0 & ~0x1fffull) | (unsigned long long)(0x1fff - (e0 + __popc(alive & ((1u << b) - 1u))));
             }
         }
-        // from here on a lane works on an even share of its wave's live
-        // points: entries e_lo .. e_lo + nloc - 1 of the wave's compact part
-        // (the later levels' loops run as long as their wave's most loaded
-        // lane, and live points cluster near the hull), with kref the index
-        // just before its first point in place of the thread's own base
-        const int per = (wtot + 63) >> 6;
-        const int lo = min(wtot, (L & 63) * per);
+        // from here on a thread works on an even share of the workgroup's
+        // live points: entries e_lo .. e_lo + nloc - 1 of the compact arrays
+        // (a later level runs as long as its most loaded thread, and live
+        // points cluster near the hull), with kref the index just before its
+        // first point in place of the thread's own base
+        const int per = (wtot + NT - 1) / NT;
+        const int lo = min(wtot, L * per);
         const int nloc = min(wtot, lo + per) - lo;
-        const int e_lo = (L >> 6) * CW + lo;
+        const int e_lo = lo;
         alive = nloc > 0 && !over ? (1u << nloc) - 1u : 0u;
         __syncthreads();
         const int kref = alive ? (int)cK[e_lo] - 1 : 0;
@@ -469,7 +481,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             }
             if (qbest) atomicMax(&qkey[qi], qbest);
             if (__syncthreads_or(lv == 0 && over)) {
-                state = 2;  // too many live points for a wave's compact part
+                state = 2;  // too many live points for the compact arrays
                 break;
             }
             // every wave reads the chords' keys: which chords found a point
