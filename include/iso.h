@@ -107,8 +107,9 @@ enum {
      * after any phase stamps: [0] violations, [1] chunk hulls rebuilt after
      * the chunk kernel gave up, [2] thread walks handed to a wave, [3] nested
      * bisections, [4] three-case searches, [5] levels checked, [6] root
-     * vertices checked.  A checked call returns ISO_ERR_INVARIANT when [0] is
-     * not zero.  Long rows only; slower. */
+     * vertices checked, [7] rounds of the second stage's bridges between
+     * neighbouring groups that dropped a group.  A checked call returns
+     * ISO_ERR_INVARIANT when [0] is not zero.  Long rows only; slower. */
     ISO_F_DEBUG_INVARIANTS = 8u,
     /* For iso_workspace_bytes only: size the workspace for a weighted call
      * (w != NULL).  Ignored by the fitting calls. */
@@ -136,9 +137,13 @@ enum {
      * handed to waves).  THREE_CASE: at the levels with a thread per merge,
      * walks are capped at 8 (r + log2 C) steps (r the tree level, C the chunk
      * size) and finished by the three-case bridge search of Lemma A.1.  The
-     * compact-array merges of short hulls are not affected. */
+     * compact-array merges of short hulls are not affected.  TREE_MERGES: the
+     * second stage merges short group hulls by the merge tree (default: the
+     * bridges between neighbouring groups, all at once, with groups that keep
+     * no vertex dropped round by round, and the tree after 8 such rounds). */
     ISO_F_WAVE_MERGES = 0x400u,
-    ISO_F_THREE_CASE = 0x800u
+    ISO_F_THREE_CASE = 0x800u,
+    ISO_F_TREE_MERGES = 0x1000u
 };
 
 /*

@@ -166,7 +166,7 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 
 constexpr uint32_t kKnownFlags = ISO_F_NOCHECK | ISO_F_DECREASING | ISO_F_COPY_CONTROL |
                                   ISO_F_DEBUG_INVARIANTS | ISO_F_WEIGHTED_HINT | ISO_F_PHASE_STAMPS |
-                                  ISO_F_WAVE_MERGES | ISO_F_THREE_CASE;
+                                  ISO_F_WAVE_MERGES | ISO_F_THREE_CASE | ISO_F_TREE_MERGES;
 
 // Launch timing (benchmarks only).
 struct Timing {
@@ -229,7 +229,8 @@ int fit_body(const T* y, const T* w, int64_t rows, int64_t n, T* out, int32_t* b
         iso::LongShape sh{rows, n, p.m, weighted, sign};
         iso::LongWs ws = long_ws(workspace, p, weighted, copy_control, rows);
         ws.sched = ((flags & ISO_F_WAVE_MERGES) ? iso::kSchedWaveAll : 0) |
-                   ((flags & ISO_F_THREE_CASE) ? iso::kSchedThreeCase : 0);
+                   ((flags & ISO_F_THREE_CASE) ? iso::kSchedThreeCase : 0) |
+                   ((flags & ISO_F_TREE_MERGES) ? iso::kSchedTreeTop : 0);
         e = iso::launch_long<T>(y, w, sh, ws, out, block_id, copy_control, st);
     }
     if (e != hipSuccess) return ISO_ERR_HIP;

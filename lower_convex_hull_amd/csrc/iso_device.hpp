@@ -895,6 +895,193 @@ __device__ __forceinline__ void merge_arrays(const Arr& ar, int32_t* cnt, int32_
     __syncthreads();
 }
 
+// ----------------------------------------------------------------------------
+// Local-bridge merge of compact hulls.  Nodes 0 .. nn-1 hold the lower hulls
+// of consecutive runs of points (node k: entries k*E .. k*E+cnt[k]-1, its
+// last vertex being node k+1's first).  Each node keeps the range of its
+// vertices between its bridges (common lower tangents) with its two
+// neighbours: from the bridge on its left, which touches it last at lc, to
+// the bridge on its right, which touches it first at rc.  A node whose range
+// is empty, or is one vertex at which the two bridges do not turn strictly
+// left, has no vertex on the hull of itself and its neighbours, so none on
+// the hull of the union: it is dropped and its neighbours are bridged
+// directly.  Once no node is dropped, the ranges joined by the bridges form a
+// convex chain (a vertex right of a bridge's last contact lies strictly above
+// the bridge's line, one left of its first contact likewise) with every point
+// on or above it: the hull of the union.  Where most of every node survives
+// (hulls of long runs of points), one round of bridges between neighbours,
+// all at once, replaces the levels of a merge tree.
+// ----------------------------------------------------------------------------
+
+// The tangent from point p (left of entries base+lo .. base+hi of a hull) to
+// those entries: the first k in lo .. hi-1 whose entry lies strictly below
+// the chord from p to entry k+1, else hi (the rightmost point of contact).
+__device__ __forceinline__ int arr_tangent(const Arr& ar, int base, int lo, int hi, Pt p) {
+    while (lo < hi) {
+        const int k = (lo + hi) >> 1;
+        if (cross3(p, ar.pt(base + k), ar.pt(base + k + 1)) > 0.0) hi = k;
+        else lo = k + 1;
+    }
+    return lo;
+}
+
+// The bridge of node L (g entries from lb) and node R (h entries from rb) by
+// one thread: a nested bisection over L (the first vertex of L whose
+// successor does not lie strictly below the line from it to its tangent point
+// on R), each step a bisection over R for the tangent (the paper's nested
+// bisection, section 3.3, on arrays).  adj: R follows L directly, so L's last
+// entry is R's first; unless the two turn convexly there, the bridge is the
+// one of L without its last entry and R without its first, which passes on or
+// below the shared point.
+// Returns (A, B): L's point of contact (the leftmost on the bridge line) and
+// R's (the rightmost); for a convex turn at the shared point, (g - 1, 1).
+__device__ __forceinline__ int2 arr_bridge(const Arr& ar, int lb, int g, int rb, int h, bool adj) {
+    int a = 0, b = g - 1, rlo = 0;
+    if (adj) {
+        if (cross3(ar.pt(lb + g - 2), ar.pt(lb + g - 1), ar.pt(rb + 1)) > 0.0) return make_int2(g - 1, 1);
+        b = g - 2;
+        rlo = 1;
+    }
+    int tb = -1;  // the tangent from L's entry b, once a step has found it
+    while (a < b) {
+        const int k = (a + b) >> 1;
+        const Pt Pk = ar.pt(lb + k);
+        const Pt Pn = ar.pt(lb + k + 1);
+        const int t = arr_tangent(ar, rb, rlo, h - 1, Pk);
+        if (cross3(Pk, Pn, ar.pt(rb + t)) > 0.0) {
+            a = k + 1;
+        } else {
+            b = k;
+            tb = t;
+        }
+    }
+    const int t = tb >= 0 ? tb : arr_tangent(ar, rb, rlo, h - 1, ar.pt(lb + a));
+    return make_int2(a, t);
+}
+
+// Merges nodes 0 .. nn-1 (E entries apart; MAXE bounds nn*E; nn <= 128) into
+// node 0 and sets cnt[0].  lc, rc, nx, pv, dead, ko: nn ints each in LDS.
+// Returns the number of rounds that dropped nodes, or -1, with the nodes
+// untouched, if nodes are still being dropped after kLocalRounds rounds.
+// Every thread of the workgroup calls it after a barrier that published the
+// nodes.
+constexpr int kLocalRounds = 8;
+template <int NT, int E, int MAXE>
+__device__ __forceinline__ int merge_local(const Arr& ar, int32_t* cnt, int nn, int32_t* lc, int32_t* rc,
+                                            int32_t* nx, int32_t* pv, int32_t* dead, int32_t* ko,
+                                            uint64_t* sr = nullptr /* phase stamps */) {
+    constexpr int T = 8;  // measured against 1, 2, 4, 16, 32, 64
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the bridges between neighbours, a team of T lanes each (the walk of
+    // Lemma 4.2 testing T candidates a step); a wave without a pair skips it
+    {
+        const int x = tid & (T - 1);
+        for (int g0 = 0; g0 < nn - 1; g0 += NT / T) {
+            const int g = g0 + tid / T;
+            if (g0 + (tid & ~63) / T < nn - 1) {
+                const bool act = g < nn - 1;
+                const int cL = act ? cnt[g] : 2, cR = act ? cnt[g + 1] : 2;
+                const int2 br = team_bridge(ar, g * E, cL, (g + 1) * E, cR, x, T, lane & ~(T - 1), act);
+                if (act && x == 0) {
+                    rc[g] = br.x;
+                    lc[g + 1] = br.y;
+                }
+            }
+        }
+        if (tid < nn) {
+            nx[tid] = tid + 1;
+            pv[tid] = tid - 1;
+            dead[tid] = 0;
+        }
+        if (tid == 0) {
+            lc[0] = 0;
+            rc[nn - 1] = cnt[nn - 1] - 1;
+        }
+    }
+    __syncthreads();
+    stamp(sr, 5);  // bridges between neighbours found
+    int round = 0;
+    for (;; ++round) {
+        // the first and last nodes keep their end points; any other node is
+        // dropped if its range is empty or a vertex without a strict turn
+        const int h = tid;
+        bool drop = false;
+        if (h > 0 && h < nn - 1 && !dead[h]) {
+            const int c = lc[h], d = rc[h];
+            if (c > d) {
+                drop = true;
+            } else if (c == d) {
+                const int p = pv[h], q = nx[h];
+                drop = !(cross3(ar.pt(p * E + rc[p]), ar.pt(h * E + c), ar.pt(q * E + lc[q])) > 0.0);
+            }
+        }
+        if (!__syncthreads_or(drop)) break;
+        if (round == kLocalRounds) return -1;  // (the same in every thread)
+        if (drop) dead[h] = 1;
+        __syncthreads();
+        // a node whose next node went bridges to the next one left (the last
+        // node is never dropped); it alone writes its rc and that node's lc
+        if (h < nn - 1 && !dead[h] && dead[nx[h]]) {
+            int q = nx[h];
+            while (dead[q]) ++q;
+            nx[h] = q;
+            pv[q] = h;
+            const int2 br = arr_bridge(ar, h * E, cnt[h], q * E, cnt[q], false);
+            rc[h] = br.x;
+            lc[q] = br.y;
+        }
+        __syncthreads();
+    }
+    stamp(sr, 6);  // ranges decided
+    if (tid < 64) {
+        // ko: kept entries before each node (two nodes a lane)
+        const int t0 = 2 * lane, t1 = t0 + 1;
+        const int v0 = t0 < nn && !dead[t0] ? rc[t0] - lc[t0] + 1 : 0;
+        const int v1 = t1 < nn && !dead[t1] ? rc[t1] - lc[t1] + 1 : 0;
+        int x = v0 + v1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(x, d);
+            if (lane >= d) x += u;
+        }
+        const int ex = x - v0 - v1;
+        if (t0 < nn) ko[t0] = ex;
+        if (t1 < nn) ko[t1] = ex + v0;
+        if (lane == 63) cnt[0] = x;  // no thread reads cnt past the last barrier
+    }
+    __syncthreads();
+    // the kept entries to the front: every one read, then written
+    constexpr int KQ = (MAXE + NT - 1) / NT;
+    double vs[KQ], vw[KQ];
+    int vt[KQ], dst[KQ];
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+        const int e = tid + q * NT;
+        dst[q] = -1;
+        if (e < nn * E) {
+            const int nd = e / E, pos = e - nd * E;
+            if (!dead[nd] && pos >= lc[nd] && pos <= rc[nd]) {
+                dst[q] = ko[nd] + pos - lc[nd];
+                vs[q] = ar.S[e];
+                vw[q] = ar.W[e];
+                vt[q] = ar.tag[e];
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+        if (dst[q] >= 0) {
+            ar.S[dst[q]] = vs[q];
+            ar.W[dst[q]] = vw[q];
+            ar.tag[dst[q]] = vt[q];
+        }
+    }
+    __syncthreads();
+    stamp(sr, 7);  // kept entries moved
+    return round;
+}
+
 // Prefix counts over a row's root list D of nroot segments (at most one per
 // chunk, in chunk order) for the reconstruction: vb[i] = root vertices before
 // segment i (block ids), and fs[j] = segments in chunks before chunk j, which

@@ -40,6 +40,9 @@ constexpr int kHardCap = 256;     // merges per level a wave may take over
 // the three-case bridge search instead of handing the merge to a wave.
 constexpr int kSchedWaveAll = 1;
 constexpr int kSchedThreeCase = 2;
+// The second stage's compact-array merge by the merge tree instead of the
+// bridges between neighbouring groups (measurement and stress only).
+constexpr int kSchedTreeTop = 4;
 
 // Debug counters (ISO_F_DEBUG_INVARIANTS), 8 x uint64 at the end of the workspace.
 constexpr int kDbgViolations = 0;   // segment-list invariants found broken
@@ -49,6 +52,7 @@ constexpr int kDbgBisect = 3;       // nested bisections (walks beyond every cap
 constexpr int kDbgThreeCase = 4;    // three-case bridge searches
 constexpr int kDbgLevels = 5;       // segment-list merge levels checked
 constexpr int kDbgRootVerts = 6;    // root vertices checked for convexity
+constexpr int kDbgLocalRounds = 7;  // rounds of the local-bridge merge that dropped groups
 constexpr int kDbgCount = 8;
 
 // Phase stamps per workgroup (ISO_F_PHASE_STAMPS).

@@ -656,6 +656,7 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
     __shared__ int4 s_hard[kHardCap];
     __shared__ int s_ilo[kTopMax], s_ihi[kTopMax], s_off[kTopMax + 1];
     __shared__ int s_gh[kTopMax], s_gn[kTopMax], s_gf[kTopMax], s_ver[kTopMax];
+    __shared__ int32_t s_lc[kTopMax], s_rc[kTopMax], s_nx[kTopMax], s_pv[kTopMax], s_dead[kTopMax], s_ko[kTopMax];
     const int64_t row = blockIdx.x;
     const int64_t rb = row * m, gb = row * ng;
     const int tid = threadIdx.x;
@@ -767,8 +768,15 @@ __global__ __launch_bounds__(kTopNT) void k_top_merge(int m, int ng, LongWs ws) 
             s_ver[g] = 0;
         }
         __syncthreads();
-        merge_arrays<NT>(ar, CNT, s_ver, ng, E, sr);
-        stamp(sr, 2);  // merge tree done (compact arrays)
+        // group hulls keep most of their vertices: bridges between
+        // neighbouring groups, all at once; the merge tree if groups are still
+        // being dropped after a few rounds
+        const bool tree = EX && (ws.sched & kSchedTreeTop) != 0;
+        const int rounds =
+            tree ? -1 : merge_local<NT, E, kTopFastMax * E>(ar, CNT, ng, s_lc, s_rc, s_nx, s_pv, s_dead, s_ko, sr);
+        if (EX && tid == 0 && !tree && rounds != 0) dbg_add(ws.dbg, kDbgLocalRounds, rounds < 0 ? kLocalRounds : rounds);
+        if (rounds < 0) merge_arrays<NT>(ar, CNT, s_ver, ng, E, sr);
+        stamp(sr, 2);  // merge done (compact arrays)
         const int hr = CNT[0];
         // one root segment per run of a chunk's vertices; its chunk into rcbuf
         uint16_t* R16 = reinterpret_cast<uint16_t*>(R);

@@ -32,6 +32,7 @@ ISO_F_COPY_CONTROL = 4
 ISO_F_DEBUG_INVARIANTS = 8
 ISO_F_WAVE_MERGES = 0x400
 ISO_F_THREE_CASE = 0x800
+ISO_F_TREE_MERGES = 0x1000
 ISO_F_WEIGHTED_HINT = 0x100
 ISO_F_PHASE_STAMPS = 0x200
 

@@ -2,7 +2,7 @@
 section 4, Definition 4.3 and Theorem 4.4, checked after every segment-list
 merge level and on every root list) and its path counters, and the
 merge-schedule variants (ISO_F_WAVE_MERGES, ISO_F_THREE_CASE: paper section
-7.4 and appendix A) against the oracle.  The counters show which merge paths a
+7.4 and appendix A; ISO_F_TREE_MERGES) against the oracle.  The counters show which merge paths a
 workload takes, so the tests below also prove that the stress data reaches
 the wave walks, the nested bisection, the three-case search and the chunk
 rebuild."""
@@ -19,7 +19,7 @@ from tests import fitcheck
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ("violations", "rebuilt", "to_wave", "bisect", "three_case", "levels", "root_vertices")
+NAMES = ("violations", "rebuilt", "to_wave", "bisect", "three_case", "levels", "root_vertices", "local_rounds")
 
 
 def say(*a):
@@ -55,12 +55,13 @@ def fit_dbg(torch, y, w=None, flags=0):
     return st, out.cpu().numpy(), dict(zip(NAMES, cnt.tolist()))
 
 
-def check(torch, y, w=None, flags=0, name=""):
+def check(torch, y, w=None, flags=0, name="", interior=True):
+    """interior: the root lists have vertices besides the row ends to check."""
     y = np.atleast_2d(np.asarray(y, np.float32))
     st, out, c = fit_dbg(torch, y, w, flags)
     say(f"[debug] {name} rows={y.shape[0]} n={y.shape[1]} flags={flags}: {c}")
     assert st == iso.ISO_OK, iso.iso_status_str(st)
-    assert c["violations"] == 0 and c["root_vertices"] > 0
+    assert c["violations"] == 0 and (c["root_vertices"] > 0 or not interior)
     _, z64, _ = oracle.fit_rows_f32(y, w)
     ok, wa, wo, r = fitcheck.parity(y, w, out, z64)
     assert ok, (name, wa, wo, r)
@@ -143,3 +144,48 @@ def test_schedule_variants(torch, variant):
         assert tot["to_wave"] == 0, tot  # thread-per-merge levels never hand over
     else:
         assert tot["to_wave"] == 0, tot
+
+
+def _cascade_row(ng):
+    """One row of ng groups of 64 chunks, each group strictly decreasing (its
+    hull the two end points), with group sums that put the first group
+    boundary low and the others on a convex parabola: every boundary but the
+    ends lies above the chord from the row's start to the next boundary, so
+    the bridges between neighbouring groups drop one group per round."""
+    L = kGroupLen
+    a, H = 1.0, 2.0 * ng * (ng + 1)
+    k = np.arange(L, dtype=np.float64)
+    y = np.empty(ng * L, np.float32)
+    for g in range(ng):
+        mean = H + a if g == 0 else a * (2 * g + 1)
+        y[g * L:(g + 1) * L] = mean + 50.0 * (0.5 - k / L)
+    return y[None, :]
+
+
+kGroupLen = 64 * 4096
+
+
+@pytest.mark.parametrize("case", ["decreasing", "cascade6", "cascade12", "noisy"])
+def test_top_merge_drops_groups_and_falls_back_to_the_tree(torch, case):
+    """The second stage's bridges between neighbouring groups: groups that keep
+    no vertex are dropped round by round (a decreasing trend drops them all at
+    once; the cascades one a round, the longer one beyond the round limit,
+    where the merge tree takes over); every result matches the oracle and,
+    bit for bit, the merge tree's (ISO_F_TREE_MERGES)."""
+    if case == "decreasing":
+        # a decreasing trend over the first groups, then an increasing one
+        rng = np.random.default_rng(71)
+        n = 9 * kGroupLen + 1234
+        y = (3.0 * np.abs(np.linspace(-0.5, 1.0, n)) + 2.0 * rng.standard_normal(n)).astype(np.float32)[None, :]
+    elif case == "noisy":
+        y, _ = inputs.noisy(1, 39 * kGroupLen - 4321, 72)
+    else:
+        y = _cascade_row(int(case[len("cascade"):]))
+    inner = not case.startswith("cascade")  # a cascade's hull is its two end points
+    out, c = check(torch, y, None, name=f"top merge {case}", interior=inner)
+    out_t, c_t = check(torch, y, None, flags=iso.ISO_F_TREE_MERGES, name=f"top merge {case}, tree", interior=inner)
+    assert np.array_equal(out, out_t)
+    assert c_t["local_rounds"] == 0
+    want = {"decreasing": lambda r: r >= 1, "cascade6": lambda r: r == 4, "cascade12": lambda r: r == 8,
+            "noisy": lambda r: r == 0}[case]
+    assert want(c["local_rounds"]), c
