@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kCalNT) void k_calib_apply(const double* __restrict
             const double a = xp[i - 1], b = xp[i];
             double t = __ddiv_rn(__dsub_rn(q, a), fmax(__dsub_rn(b, a), 1e-300));
             t = fmin(fmax(t, 0.0), 1.0);
-            v = __dadd_rn(fp[i - 1], __dmul_rn(t, __dsub_rn(fp[i], fp[i - 1])));
+            v = __dadd_rn(fp[i - 1], mul_rn(t, __dsub_rn(fp[i], fp[i - 1])));
         }
         out[j] = v;
     }

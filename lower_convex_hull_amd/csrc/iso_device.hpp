@@ -28,7 +28,7 @@ __device__ __forceinline__ uint64_t* stamp_row(uint64_t* area, int64_t wg) {
 // The two products are rounded separately (no fused multiply-add), so a
 // repeated point or an exactly collinear triple gives exactly 0.
 __device__ __forceinline__ double cross3(Pt a, Pt b, Pt c) {
-    return __dmul_rn(b.w - a.w, c.s - a.s) - __dmul_rn(b.s - a.s, c.w - a.w);
+    return mul_rn(b.w - a.w, c.s - a.s) - mul_rn(b.s - a.s, c.w - a.w);
 }
 
 // Makes one lane's LDS writes visible to the other lanes of its wave and keeps
@@ -426,14 +426,14 @@ __device__ __forceinline__ Bridge three_case_bridge(const V X, const List<DT> Lq
         const double daw = A1.w - A0.w, das = A1.s - A0.s;
         const double dbw = B1.w - B0.w, dbs = B1.s - B0.s;
         const double lrw = (B0.w + B1.w) - (A0.w + A1.w), lrs = (B0.s + B1.s) - (A0.s + A1.s);
-        const bool c1 = __dmul_rn(das, lrw) >= __dmul_rn(lrs, daw);  // slope(alpha) >= slope(lr)
-        const bool c2 = __dmul_rn(lrs, dbw) >= __dmul_rn(dbs, lrw);  // slope(lr) >= slope(beta)
+        const bool c1 = mul_rn(das, lrw) >= mul_rn(lrs, daw);  // slope(alpha) >= slope(lr)
+        const bool c2 = mul_rn(lrs, dbw) >= mul_rn(dbs, lrw);  // slope(lr) >= slope(beta)
         if (c1) a1 = am;
         if (c2) b0 = bn;
         if (!c1 && !c2) {
-            const double ca = __dmul_rn(A0.s, daw) - __dmul_rn(das, A0.w);
-            const double cb = __dmul_rn(B0.s, dbw) - __dmul_rn(dbs, B0.w);
-            const double D = __dmul_rn(ca, dbw) - __dmul_rn(cb, daw);
+            const double ca = mul_rn(A0.s, daw) - mul_rn(das, A0.w);
+            const double cb = mul_rn(B0.s, dbw) - mul_rn(dbs, B0.w);
+            const double D = mul_rn(ca, dbw) - mul_rn(cb, daw);
             if (D <= 0.0) a0 = an;
             if (D >= 0.0) b1 = bm;
         }

@@ -361,7 +361,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
 #pragma unroll
             for (int b = 0; b < P; ++b) {
                 const int k = base + b + 1;
-                const double c = __dmul_rn(WT ? pw[b] : (double)k, B.s) - __dmul_rn(ps[b], B.w);
+                const double c = mul_rn(WT ? pw[b] : (double)k, B.s) - mul_rn(ps[b], B.w);
                 const bool live = ((alive >> b) & 1u) && c > 0.0;
                 if (!live) alive &= ~(1u << b);
                 const unsigned long long key = live ? mkkey(c, b) : 0ull;
@@ -468,7 +468,7 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
                         dW = sm.qW[cb][i + 1] - Aw;
                         dS = sm.qS[cb][i + 1] - As;
                     }
-                    const double c = __dmul_rn(Wk - Aw, dS) - __dmul_rn(Sk - As, dW);
+                    const double c = mul_rn(Wk - Aw, dS) - mul_rn(Sk - As, dW);
                     const bool better = c > bc;  // bc >= 0, so a better point is live
                     alive = c > 0.0 ? alive : (alive & ~(1u << b));
                     bc = better ? c : bc;

@@ -8,6 +8,15 @@
 
 namespace iso {
 
+// An f64 product rounded on its own: the compiler may not fuse it with a
+// neighbouring addition into a multiply-add (HIP's __dmul_rn is a plain
+// product, which it may fuse).  Cross products built from two of these give
+// exactly zero whenever the two products are equal.
+__device__ __forceinline__ double mul_rn(double a, double b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 // Long rows are cut into chunks of kChunk points, one 256-thread workgroup
 // each (16 points per thread).  Rows up to kShortMax elements are fitted whole
 // by one workgroup and never touch the workspace.

@@ -1035,7 +1035,7 @@ __global__ __launch_bounds__(256) void k_debug_root(int m, LongWs ws) {
             ++bad;
             continue;
         }
-        const double t1 = __dmul_rn(b.w - a.w, c.s - a.s), t2 = __dmul_rn(b.s - a.s, c.w - a.w);
+        const double t1 = mul_rn(b.w - a.w, c.s - a.s), t2 = mul_rn(b.s - a.s, c.w - a.w);
         // a right turn beyond rounding: the chain is not convex there
         if (t1 - t2 < -1e-9 * (fabs(t1) + fabs(t2))) ++bad;
         if (!(b.w > a.w)) ++bad;

@@ -495,3 +495,30 @@ def test_fit_wrapper_on_torch_stream(torch):
     s.synchronize()
     _, z64, _ = oracle.fit_rows_f32(y)
     assert fitcheck.parity(y, None, out.cpu().numpy(), z64)[0]
+
+
+def test_constant_runs_are_single_blocks(torch):
+    """Increasing runs of one f32 value each (values in [0.5, 1), not dyadic
+    fractions with few bits): the points of a run are exactly collinear in the
+    cumulative sum diagram (every S is an exact f64 sum here), so each run is
+    one block, as the oracle pools equal means.  The hull predicates must
+    round both products of a cross product on their own: a fused
+    multiply-add leaves the rounding error of one product instead of zero,
+    which shows on runs long enough for the products to need more than 53
+    bits."""
+    rng = np.random.default_rng(81)
+    for rows, n, most in ((4, 3000, 8), (1, 300_000, 750), (1, 3_000_000, 7500), (1, 3_000_000, 1_000_000)):
+        y = np.empty((rows, n), np.float32)
+        for r in range(rows):
+            lens = rng.integers(1, most, size=n)
+            starts = np.concatenate([[0], np.cumsum(lens)])
+            nr = int(np.searchsorted(starts, n)) + 1
+            vals = (0.5 + 0.49 * np.arange(nr) / nr).astype(np.float32)
+            run = np.searchsorted(starts, np.arange(n), side="right") - 1
+            y[r] = vals[run]
+        st, out, bid = gpu_fit(torch, y)
+        assert st == iso.ISO_OK, iso.iso_status_str(st)
+        _, z64, obid = oracle.fit_rows_f32(y)
+        assert fitcheck.parity(y, None, out, z64)[0], n
+        for r in range(rows):
+            assert np.array_equal(bid[r], obid[r]), (n, r, int(bid[r].max()), int(obid[r].max()))
