@@ -154,6 +154,8 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     constexpr int G = C / (4 * NT);  // groups of 4 consecutive elements per thread
     __shared__ int vidx[kExpTile + 1];
     __shared__ T vslope[kExpTile + 1];
+    __shared__ double spS[NT], spW[WT ? NT : 1];
+    __shared__ int spI[NT];
     __shared__ ChunkRec s_rc;
     __shared__ int s_inc, s_nan;
     const int64_t gid = blockIdx.x;
@@ -190,6 +192,18 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             }
         }
     };
+    // the chunk's first NT slot entries (every hull quickhull builds fits),
+    // read while thread 0 forms the record, so that a short surviving range
+    // needs no further global read (a strictly increasing chunk has no slot)
+    if (!(ws.chunk_flag[gid] & kChunkInc)) {
+        const size_t s0 = (size_t)gid * (C + 1) + tid;
+        const int si = ws.slot_idx[s0];
+        const double ss = ws.slot_S[s0];
+        const double sw = WT ? ws.slot_W[s0] : 0.0;
+        spI[tid] = si;
+        spS[tid] = ss;
+        if (WT) spW[tid] = sw;
+    }
     if (tid == 0) {
         // the row's flags, the chunk's flags and its first root segment, read
         // together; then the record
@@ -298,8 +312,18 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
         return sg * (T)(ds / dw);
     };
     if (nv <= kExpTile) {
-        for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
-        for (int v = tid; v + 1 < nv; v += NT) vslope[v] = edge_slope(v);
+        if (rc.hi < NT) {
+            // the surviving range lies in the entries read at the start
+            if (tid < nv) vidx[tid] = spI[rc.lo + tid];
+            if (tid + 1 < nv) {
+                const int v = rc.lo + tid;
+                const double dw = WT ? spW[v + 1] - spW[v] : (double)(spI[v + 1] - spI[v]);
+                vslope[tid] = sg * (T)((spS[v + 1] - spS[v]) / dw);
+            }
+        } else {
+            for (int v = tid; v < nv; v += NT) vidx[v] = ws.slot_idx[slot + v];
+            for (int v = tid; v + 1 < nv; v += NT) vslope[v] = edge_slope(v);
+        }
         __syncthreads();
         // q = number of the chunk's surviving vertices at or before each
         // group's first element: the groups' searches step together, one LDS
