@@ -192,10 +192,35 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             }
         }
     };
-    // the chunk's first NT slot entries (every hull quickhull builds fits),
-    // read while thread 0 forms the record, so that a short surviving range
-    // needs no further global read (a strictly increasing chunk has no slot)
-    if (!(ws.chunk_flag[gid] & kChunkInc)) {
+    // read while thread 0 forms the record: a strictly increasing chunk's
+    // input (its fit is mostly its own elements), else the chunk's first NT
+    // slot entries (every hull quickhull builds fits), so that a short
+    // surviving range needs no further global read
+    const bool incc = (ws.chunk_flag[gid] & kChunkInc) != 0;
+    const T* gy = static_cast<const T*>(ws.y) + off;
+    const bool vy = vec && (((uintptr_t)gy) & 15u) == 0;
+    T ya[G][4];
+    if (incc) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int e0 = 4 * (g * NT + tid);
+            if (vy && e0 + 4 <= len) {
+                if constexpr (sizeof(T) == 4) {
+                    typedef float f4v __attribute__((ext_vector_type(4)));
+                    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gy + e0));
+                    ya[g][0] = t.x; ya[g][1] = t.y; ya[g][2] = t.z; ya[g][3] = t.w;
+                } else {
+                    typedef double d2v __attribute__((ext_vector_type(2)));
+                    const d2v t0 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0));
+                    const d2v t1 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0 + 2));
+                    ya[g][0] = t0.x; ya[g][1] = t0.y; ya[g][2] = t1.x; ya[g][3] = t1.y;
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) ya[g][t] = e0 + t < len ? gy[e0 + t] : T(0);
+            }
+        }
+    } else {
         const size_t s0 = (size_t)gid * (C + 1) + tid;
         const int si = ws.slot_idx[s0];
         const double ss = ws.slot_S[s0];
@@ -209,7 +234,6 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
         // together; then the record
         const int64_t rb = row * m;
         const int rf = ws.row_flag[row];
-        const int cf = ws.chunk_flag[gid];
         const int fsj = rec_done ? 0 : ws.node_cnt[rb + j];
         const int nrb = rec_done ? 0 : ws.root_n[row];
         ChunkRec r{};
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
             r = chunk_record(X, ws.desc_scr + rb, nrb, ws.vb + rb, fsj, ws.rslope + rb, j);
         }
         s_rc = r;
-        s_inc = (cf & kChunkInc) != 0;
+        s_inc = incc;
         s_nan = (rf & kFlagNonfinite) != 0;
     }
     __syncthreads();
@@ -259,32 +283,9 @@ __global__ __launch_bounds__(kExpNT) void k_expand(int64_t n, int m, float sign,
     if (s_inc) {
         // every point of the chunk is a vertex at its own index: an element
         // between two surviving vertices is its own edge, so its fit is its
-        // value; elements before or after the surviving range take the edges
-        // into and out of it
-        const T* gy = static_cast<const T*>(ws.y) + off;
-        const bool vy = vec && (((uintptr_t)gy) & 15u) == 0;
+        // value (read at the start); elements before or after the surviving
+        // range take the edges into and out of it
         const T sin_ = sg * (T)rc.slope_in, sout = sg * (T)rc.slope_out;
-        // every load first, then the stores
-        T ya[G][4];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int e0 = 4 * (g * NT + tid);
-            if (vy && e0 + 4 <= len) {
-                if constexpr (sizeof(T) == 4) {
-                    typedef float f4v __attribute__((ext_vector_type(4)));
-                    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gy + e0));
-                    ya[g][0] = t.x; ya[g][1] = t.y; ya[g][2] = t.z; ya[g][3] = t.w;
-                } else {
-                    typedef double d2v __attribute__((ext_vector_type(2)));
-                    const d2v t0 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0));
-                    const d2v t1 = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(gy + e0 + 2));
-                    ya[g][0] = t0.x; ya[g][1] = t0.y; ya[g][2] = t1.x; ya[g][3] = t1.y;
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) ya[g][t] = e0 + t < len ? gy[e0 + t] : T(0);
-            }
-        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int e0 = 4 * (g * NT + tid);
