@@ -19,7 +19,10 @@ namespace {
 // lists and starts in LDS.  Stage 2: one workgroup per row merges the group
 // hulls (the upper levels) with the group windows in LDS; a vertex outside a
 // group window is found through the group's segment list.  Every walk step
-// then reads LDS instead of a chain of cache misses.
+// then reads LDS instead of a chain of cache misses.  Where every group hull
+// fits its window, stage 2 bridges all neighbouring groups at once instead of
+// running the upper levels (merge_local: each group keeps the vertices
+// between its two bridges, and groups that keep none are dropped).
 // ----------------------------------------------------------------------------
 
 // Schedule, debug counters and tree level of one segment-list merge level.
