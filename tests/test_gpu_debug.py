@@ -2,10 +2,11 @@
 section 4, Definition 4.3 and Theorem 4.4, checked after every segment-list
 merge level and on every root list) and its path counters, and the
 merge-schedule variants (ISO_F_WAVE_MERGES, ISO_F_THREE_CASE: paper section
-7.4 and appendix A; ISO_F_TREE_MERGES) against the oracle.  The counters show which merge paths a
-workload takes, so the tests below also prove that the stress data reaches
-the wave walks, the nested bisection, the three-case search and the chunk
-rebuild."""
+7.4 and appendix A; ISO_F_TREE_MERGES) against the oracle.  The counters
+show which merge paths a workload takes, so the tests below also prove that
+the stress data reaches the wave walks, the nested bisection, the three-case
+search, the chunk rebuild, and the second stage's group drops and its tree
+fallback."""
 from __future__ import annotations
 
 import sys
