@@ -522,3 +522,31 @@ def test_constant_runs_are_single_blocks(torch):
         assert fitcheck.parity(y, None, out, z64)[0], n
         for r in range(rows):
             assert np.array_equal(bid[r], obid[r]), (n, r, int(bid[r].max()), int(obid[r].max()))
+
+
+def test_random_long_rows_against_oracle(torch):
+    """Seeded random long rows of 2 to 30 groups of 64 chunks: trends up and
+    down (so that the second stage's bridges between neighbouring groups drop
+    groups in some rows), V shapes, steps and sawtooths, with and without
+    weights, each against the oracle."""
+    G = 64 * 4096
+    rng = np.random.default_rng(97)
+    for case in range(16):
+        n = int(rng.integers(2 * G, 30 * G)) + int(rng.integers(0, 4096))
+        kind = ("trend", "vee", "steps", "saw")[case % 4]
+        t = np.linspace(0.0, 1.0, n)
+        sd = float(rng.uniform(0.1, 3.0))
+        if kind == "trend":
+            y = float(rng.uniform(-3, 3)) * t + sd * rng.standard_normal(n)
+        elif kind == "vee":
+            y = 3.0 * np.abs(t - float(rng.uniform(0.2, 0.8))) + sd * rng.standard_normal(n)
+        elif kind == "steps":
+            k = int(rng.integers(2, 40))
+            y = np.repeat(rng.normal(0, 1, k), -(-n // k))[:n] + 0.1 * sd * rng.standard_normal(n)
+        else:
+            period = int(rng.integers(1000, n // 3))
+            y = (np.arange(n) % period) / period + 0.1 * sd * rng.standard_normal(n)
+        y = y.astype(np.float32)[None, :]
+        w = inputs.weights(("none", "uniform", "exp")[case % 3], n, case)
+        check(torch, y, None if w is None else w[None, :], name=f"random {case} {kind} n={n}",
+              block_ids=True)
