@@ -399,7 +399,9 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
         raw[q] = i < nraw ? wsrc[i] : make_double2(0.0, 0.0);
     }
     double ts = 0.0, tw = 0.0;
+    int cdf = 0;  // the chunk's data flags (a rebuild below leaves them as they are)
     if (wid == 0 && wlane < gc) {
+        cdf = ws.chunk_flag[rb + j0 + wlane] & kFlagData;
         ts = ws.tot_S[rb + j0 + wlane];
         if (WT) tw = ws.tot_W[rb + j0 + wlane];
     }
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(kGroupNT) void k_group_merge(int m, int ng, LongWs 
     }
     if (wid == 0) {
         // the group's data flags, for the second stage
-        int f = wlane < gc ? (ws.chunk_flag[rb + j0 + wlane] & kFlagData) : 0;
+        int f = cdf;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) f |= __shfl_xor(f, d);
         if (wlane == 0) gwo->flags = f;
