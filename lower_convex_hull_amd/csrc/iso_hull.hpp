@@ -50,8 +50,8 @@ struct HullSmem {
     // room for CW entries per wave; the region arrays serve where they
     // exist), each wave's count of them, the vertex list
     // (two buffers), and per chord the key of the farthest point below it
-    static constexpr int CW = MODE == kHullQuick ? kQhWaveCap : 64 * RS;
-    static constexpr int NC = MODE == kHullQuick ? (NT / 64) * kQhWaveCap : 1;
+    static constexpr int CW = MODE == kHullQuick ? (WT ? kQhWaveCapW : kQhWaveCap) : 64 * RS;
+    static constexpr int NC = MODE == kHullQuick ? (NT / 64) * CW : 1;
     double cS[NC];
     double cW[WT ? NC : 1];
     uint16_t ck[NC];
@@ -330,6 +330,30 @@ __device__ __forceinline__ HullOut block_hull(HullSmem<NT, P, WT, MODE>& sm, con
             // keeps it)
             const T nxt = __shfl_down(yv[0], 1);
             if ((L & 63) != 63 && base + P < len && !(yv[P - 1] < nxt)) alive &= ~(1u << (P - 1));
+        }
+        if constexpr (WT && MODE == kHullQuick) {
+            // weighted: a vertex also lies strictly below the chord between
+            // the points two before and two after it, which drops about a
+            // quarter of the candidates and keeps the compact arrays (sized
+            // for four workgroups per CU) from overflowing.  Lanes at a
+            // wave's ends and points near the block's ends skip the test.
+            const int lane = L & 63;
+            const double pS2 = __shfl_up(ps[P - 2], 1), pW2 = __shfl_up(pw[P - 2], 1);
+            const double nS0 = __shfl_down(ps[0], 1), nW0 = __shfl_down(pw[0], 1);
+            const double nS1 = __shfl_down(ps[1], 1), nW1 = __shfl_down(pw[1], 1);
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                const int k = base + b + 1;
+                bool ok = k - 2 >= 0 && k + 2 <= len && (b >= 1 || lane > 0 || L == 0) &&
+                          (b <= P - 3 || lane < 63);
+                if (b == 0 && L == 0) ok = false;  // point -1 does not exist
+                if (ok && ((alive >> b) & 1u)) {
+                    const Pt Pm = b >= 2 ? Pt{pw[b - 2], ps[b - 2]} : (b == 1 ? Pt{w0, s0} : Pt{pW2, pS2});
+                    const Pt Pp = b <= P - 3 ? Pt{pw[b + 2], ps[b + 2]}
+                                             : (b == P - 2 ? Pt{nW0, nS0} : Pt{nW1, nS1});
+                    if (!(cross3(Pm, Pt{pw[b], ps[b]}, Pp) > 0.0)) alive &= ~(1u << b);
+                }
+            }
         }
         if (L == 0) {
             sm.qk[0][0] = 0;

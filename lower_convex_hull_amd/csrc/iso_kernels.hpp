@@ -26,6 +26,7 @@ constexpr int kChunk = kLongNT * kLongP;  // 4096
 constexpr int kShortMax = 4096;
 constexpr int kQhMax = 64;          // vertices of a block hull built by quickhull
 constexpr int kQhWaveCap = 576;     // room per wave for the live points after quickhull's first level (chunk kernel)
+constexpr int kQhWaveCapW = 512;    // the same, weighted (four workgroups per CU fit the LDS)
 constexpr int kQhLevels = 10;       // quickhull levels before the chains-and-merges fallback
 constexpr int kRedoGrid = 768;      // workgroups of the fallback chunk kernel (3 per CU)
 constexpr int kExpTile = 512;       // surviving vertices of a chunk the expansion keeps in LDS

@@ -190,3 +190,19 @@ def test_top_merge_drops_groups_and_falls_back_to_the_tree(torch, case):
     want = {"decreasing": lambda r: r >= 1, "cascade6": lambda r: r == 4, "cascade12": lambda r: r == 8,
             "noisy": lambda r: r == 0}[case]
     assert want(c["local_rounds"]), c
+
+
+def test_weighted_noisy_chunks_fit_the_compact_arrays(torch):
+    """Weighted chunks keep fewer live points in LDS (room for 512 a wave, so
+    that four workgroups fit a CU); the extra test of each candidate against
+    the chord two points away keeps noisy weighted rows inside that room: no
+    chunk is rebuilt.  A steep trend inside every chunk may overflow it; the
+    rebuilt chunks then still give the oracle's fit."""
+    n = 2_000_000 + 77
+    y, _ = inputs.noisy(1, n, 81)
+    for kind in ("uniform", "exp"):
+        w = inputs.weights(kind, n, 82)[None, :]
+        _, c = check(torch, y, w, name=f"noisy weighted {kind}")
+        assert c["rebuilt"] == 0, c
+    steep = (np.linspace(0, 5000, n) + np.random.default_rng(83).standard_normal(n)).astype(np.float32)[None, :]
+    check(torch, steep, inputs.weights("uniform", n, 84)[None, :], name="steep weighted")
