@@ -424,7 +424,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across "
-              "GPUs with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
