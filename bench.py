@@ -423,7 +423,7 @@ def say(*a):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across "
+        print("bench.py measures one GPU: the library has no multi-GPU path (rows shard across "
               "GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
